@@ -1,0 +1,289 @@
+#!/usr/bin/env python3
+"""Benchmark of paged MLA decode over FP8 / NVFP4 latent KV on one MI355X.
+
+One step = one decode call over the whole batch: the split-KV kernel (page-table gather,
+in-register dequantization, QK^T and PV on MFMA, online softmax, split partials) and the
+merge kernel, i.e. one layer of one decode step for every request.  Inputs are synthetic
+(synth.py) and resident in HBM before the timed region.  Consecutive steps cycle through
+several copies of the pool ("layers") at different addresses, so that the 256 MB
+Infinity Cache cannot serve a step from the previous one.
+
+Default workload: FP8 pool of the pages (495,552 tokens x 576), batch 8, 32K context, page 64.
+Other workloads (--workload): nvfp4_32k, nvfp4_160k, nvfp4_1m (the last one adds the
+8,192-token NVFP4 quantize-on-write to every step).
+
+Prints ONE JSON line.  `value` = KV bytes read per step / measured time per step (GB/s).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode KV-read GB/s (% of HBM peak) and decode-attn steps/s, FP8 vs NVFP4"
+HBM_PEAK_GBS = 8000.0
+FP8_ROW, NV_ROW, BF16_ROW = 576, 324, 1152
+
+
+def _hip():
+    """The HIP runtime already loaded by torch (one runtime per process)."""
+    path = next(l.split()[-1] for l in open("/proc/self/maps") if "libamdhip64" in l)
+    lib = ctypes.CDLL(path)
+    lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return lib
+
+
+class Events:
+    def __init__(self, hip, n):
+        self.hip = hip
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert hip.hipEventCreate(ctypes.byref(e)) == 0
+            self.ev.append(e.value)
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(out), self.ev[a], self.ev[b]) == 0
+        return out.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+
+
+def src_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("decode.hip", "device_common.h", "mlaq_kernels.h"):
+        h.update(open(os.path.join(ROOT, "quantized_kv_paged_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def timed_steps(step, n_layers, steps, warmup, hip, torch, profile=True):
+    """Run warmup + timed steps; returns (ms per step, split-kernel ms, merge ms)."""
+    import quantized_kv_paged_amd as qk
+    for i in range(warmup):
+        step(i % n_layers)
+    torch.cuda.synchronize()
+    ev = Events(hip, 3 * steps) if profile else None
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        if profile:
+            qk.mlaq_set_profile_events(ev.ev[3 * i], ev.ev[3 * i + 1], ev.ev[3 * i + 2])
+        step(i % n_layers)
+    end.record()
+    torch.cuda.synchronize()
+    total = start.elapsed_time(end) / steps
+    split = merge = None
+    if profile:
+        split = float(np.mean([ev.ms(3 * i, 3 * i + 1) for i in range(steps)]))
+        merge = float(np.mean([ev.ms(3 * i + 1, 3 * i + 2) for i in range(steps)]))
+        ev.close()
+    return total, split, merge
+
+
+def pmc_traffic(kernel_tag: str, launches_bytes: float):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if they were taken on
+    the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", f"{kernel_tag}_pmc.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("src_hash") != src_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, pt, pool_fp8, nvfp4=False):
+    """The oracle, as it stands, on one request of the batch (a bounded sample).  For NVFP4
+    workloads the sample's rows are first quantized by the oracle's encoder (untimed), so the
+    timed part is the decode the GPU step performs: gather, dequantize, attention."""
+    from oracle import attention, codecs
+    from oracle import nvfp4 as onv
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count()
+    b = 0
+    L = int(pt.kv_lens[b])
+    if w.kv_len > 200000:
+        L = 131072                       # bound the sample: the first 128K tokens of request 0
+    rows = attention.gather_rows(pt.kv_indptr, pt.kv_indices, w.page_size, b, L)
+    if nvfp4:
+        nv_data, nv_scales = onv.quantize_fp8_rows(pool_fp8[rows], 1.0, 1.0)
+    t0 = time.perf_counter()
+    rows = attention.gather_rows(pt.kv_indptr, pt.kv_indices, w.page_size, b, L)
+    if not nvfp4:
+        x = onv.dequant_fp8_f64(pool_fp8[rows], 1.0)
+    else:
+        x = onv.dequant_nvfp4_f64(nv_data, nv_scales, 1.0)
+    q = codecs.bf16_bits_to_f64(synth.q_bits(w.seed, w.batch, w.heads))[b]
+    attention.decode_dense(q, x, w.sm_scale)
+    dt = time.perf_counter() - t0
+    row = NV_ROW if nvfp4 else FP8_ROW
+    return {"value": round(L * row / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"request 0, first {L} tokens of {w.kv_len}: gather + fp64 dequant + fp64 attention "
+                      f"({dt:.2f} s wall)",
+            "steps_per_s": round(1.0 / (dt * (w.batch * w.kv_len) / L), 6)}
+
+
+def build_pools(w, torch, qk, n_layers, fmt):
+    """Device pools for n_layers layers (copies at distinct addresses) + page table + q."""
+    import synth
+    t0 = time.perf_counter()
+    pt = synth.page_table(w)
+    host = synth.build_fp8_pool(w, pt)
+    t1 = time.perf_counter()
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    d = {"indptr": dev(pt.kv_indptr), "indices": dev(pt.kv_indices), "lens": dev(pt.kv_lens),
+         "q": dev(synth.q_bits(w.seed, w.batch, w.heads).view(np.int16)).view(torch.bfloat16)}
+    fp8 = dev(host)
+    d["fp8"] = [fp8] + [fp8.clone() for _ in range(n_layers - 1)] if fmt == "fp8" else [fp8]
+    if fmt == "nvfp4":
+        data = torch.empty((w.pool_tokens, 288), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((w.pool_tokens, 36), dtype=torch.uint8, device="cuda")
+        slots = torch.arange(w.pool_tokens, dtype=torch.int64, device="cuda")
+        qk.kv_quantize_nvfp4(fp8, qk.MLAQ_FP8_E4M3, 1.0, slots, data, scales, 1.0)
+        d["nv"] = [(data, scales)] + [(data.clone(), scales.clone()) for _ in range(n_layers - 1)]
+        del slots
+    torch.cuda.synchronize()
+    d["gen_s"] = round(t1 - t0, 1)
+    return pt, host, d
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="fp8_32k", choices=["fp8_32k", "nvfp4_32k", "nvfp4_160k", "nvfp4_1m"])
+    ap.add_argument("--layers", type=int, default=0, help="pool copies cycled through (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the comparison legs")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import quantized_kv_paged_amd as qk
+    import synth
+    torch.cuda.set_device(0)
+    hip = _hip()
+    w = synth.WORKLOADS[args.workload]
+    fmt = w.fmt
+    live = w.batch * w.kv_len * (FP8_ROW if fmt == "fp8" else NV_ROW)
+    n_layers = args.layers or max(2, int(np.ceil(600e6 / live)))
+    print(f"[bench] {w.name}: building {n_layers} layer pools", file=sys.stderr, flush=True)
+    pt, host, d = build_pools(w, torch, qk, n_layers, fmt)
+    print(f"[bench] pools ready (host generation {d['gen_s']} s)", file=sys.stderr, flush=True)
+
+    p = qk.decode_params(w.batch, w.heads, w.page_size, w.kv_len, w.pool_tokens, w.sm_scale)
+    splits = qk.mlaq_decode_num_splits(p)
+    ws = torch.zeros(max(qk.mlaq_decode_workspace_bytes(p), 256), dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.batch, w.heads, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.batch, w.heads), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    pp = ctypes.byref(p)
+    L = qk._lib
+    common = (d["indptr"].data_ptr(), d["indices"].data_ptr(), d["lens"].data_ptr(), out.data_ptr(),
+              lse.data_ptr(), ws.data_ptr(), ws.numel(), stream)
+    qp = d["q"].data_ptr()
+
+    def check(st):
+        if st != 0:
+            raise RuntimeError(qk.last_error())
+
+    if fmt == "fp8":
+        fp8p = [t.data_ptr() for t in d["fp8"]]
+        step = lambda l: check(L.mla_decode_fp8(pp, qp, fp8p[l], 1.0, *common))
+        kv_bytes = w.batch * w.kv_len * FP8_ROW
+    else:
+        nvp = [(a.data_ptr(), s.data_ptr()) for a, s in d["nv"]]
+        if w.write_tokens:
+            wsrc = torch.from_numpy(synth.write_source_fp8(w)).cuda()
+            wslots = torch.from_numpy(synth.slot_mapping(w, pt)).cuda()
+
+            def step(l):
+                check(L.kv_quantize_nvfp4(wsrc.data_ptr(), qk.MLAQ_FP8_E4M3, 1.0, w.write_tokens,
+                                          wslots.data_ptr(), nvp[l][0], nvp[l][1], w.pool_tokens, 1.0, stream))
+                check(L.mla_decode_nvfp4(pp, qp, nvp[l][0], nvp[l][1], 1.0, *common))
+        else:
+            step = lambda l: check(L.mla_decode_nvfp4(pp, qp, nvp[l][0], nvp[l][1], 1.0, *common))
+        kv_bytes = w.batch * w.kv_len * NV_ROW
+
+    ms, split_ms, merge_ms = timed_steps(step, n_layers, args.steps, args.warmup, hip, torch)
+    achieved = kv_bytes / (split_ms * 1e-3) / 1e9
+    value = kv_bytes / (ms * 1e-3) / 1e9
+    kernel_tag = f"mla_decode_kernel_{fmt}_{w.name}"
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": f"{w.name}: {fmt.upper()} paged MLA decode, batch {w.batch} x {w.heads} heads, "
+                               f"context {w.kv_len}, page {w.page_size}, pool {w.pool_tokens} x 576"
+                               + (f", plus quantize-on-write of {w.write_tokens} tokens" if w.write_tokens else ""),
+                   "kv_format": fmt, "batch": w.batch, "heads": w.heads, "kv_len": w.kv_len,
+                   "page_size": w.page_size, "pool_tokens": w.pool_tokens, "num_splits": splits,
+                   "layers_cycled": n_layers, "kv_bytes_per_step": kv_bytes},
+        "steps_per_s": round(1000.0 / ms, 1),
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "kernels_us": {"split": round(split_ms * 1e3, 2), "merge": round(merge_ms * 1e3, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": pmc_traffic(kernel_tag, kv_bytes), "kernel": "mla_decode_kernel",
+                     "bytes_per_launch": kv_bytes},
+    }
+
+    if not args.no_extras and fmt == "fp8":
+        # the same batch, requantized to NVFP4 with the library's own write path
+        nv_live = w.batch * w.kv_len * NV_ROW
+        nl = max(2, int(np.ceil(600e6 / nv_live)))
+        data = torch.empty((w.pool_tokens, 288), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((w.pool_tokens, 36), dtype=torch.uint8, device="cuda")
+        slots = torch.arange(w.pool_tokens, dtype=torch.int64, device="cuda")
+        qk.kv_quantize_nvfp4(d["fp8"][0], qk.MLAQ_FP8_E4M3, 1.0, slots, data, scales, 1.0)
+        nvs = [(data, scales)] + [(data.clone(), scales.clone()) for _ in range(nl - 1)]
+        nvp = [(a.data_ptr(), s.data_ptr()) for a, s in nvs]
+        nstep = lambda l: check(L.mla_decode_nvfp4(pp, qp, nvp[l][0], nvp[l][1], 1.0, *common))
+        nms, nsplit, nmerge = timed_steps(nstep, nl, args.steps, args.warmup, hip, torch)
+        res["nvfp4_same_batch"] = {"ms_per_step": round(nms, 5), "steps_per_s": round(1000 / nms, 1),
+                                   "kv_gbs": round(nv_live / (nms * 1e-3) / 1e9, 1),
+                                   "split_kernel_gbs": round(nv_live / (nsplit * 1e-3) / 1e9, 1),
+                                   "speedup_vs_fp8": round(ms / nms, 3)}
+        del nvs, data, scales
+        # the pages' path: cast the whole FP8 pool to BF16 every layer, then a 16-bit decode
+        bf = torch.empty((w.pool_tokens, 576), dtype=torch.bfloat16, device="cuda")
+        fp8p = [t.data_ptr() for t in d["fp8"]]
+
+        def cstep(l):
+            check(L.kv_dequantize(qk.MLAQ_FP8_E4M3, fp8p[l], None, 1.0, None, w.pool_tokens, w.pool_tokens,
+                                  qk.MLAQ_BF16, bf.data_ptr(), stream))
+            check(L.mla_decode_bf16(pp, qp, bf.data_ptr(), *common))
+        cms, _, _ = timed_steps(cstep, n_layers, max(20, args.steps // 4), 5, hip, torch, profile=False)
+        res["cast_baseline"] = {"ms_per_step": round(cms, 5), "steps_per_s": round(1000 / cms, 1),
+                                "bytes_moved_per_step": w.pool_tokens * (FP8_ROW + BF16_ROW) + w.batch * w.kv_len * BF16_ROW,
+                                "speedup_of_fp8_path": round(cms / ms, 2)}
+        del bf
+
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, pt, host, nvfp4=(fmt == "nvfp4"))
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,156 @@
+/* mlaq.h -- paged MLA decode over an FP8 / NVFP4 latent KV pool on MI355X (gfx950).
+ *
+ * A small C ABI.  Pointers are DEVICE pointers unless marked (host).  The caller owns
+ * all memory: queries, pools, page table, lengths, outputs and the workspace.  Calls
+ * are asynchronous on `stream`; they never allocate, never synchronise the device and
+ * never read device memory on the host.  Every argument that can be checked on the
+ * host is checked before any launch; a non-OK status means nothing was launched and
+ * mlaq_last_error() (thread-local) says why.
+ *
+ * What the calls compute, and where the pages say so:
+ *   - single-token decode attention of `num_heads` absorbed MLA queries over the latent
+ *     KV rows of each request, reached through a CSR page table (kv_indptr / kv_indices
+ *     / kv_lens), no causal mask, softmax scale sm_scale: the FlashInfer MLA decode
+ *     plan of "The Smoking Gun: Tracing the FP8-to-BF16 KV Cache Cast" (section
+ *     "Message Overview": plan(qo_indptr, kv_indptr, kv_indices, kv_len_arr,
+ *     num_local_heads, kv_lora_rank, qk_rope_head_dim, 1, False, sm_scale, q dtype,
+ *     kv dtype));
+ *   - the latent row is 576 = kv_lora_rank 512 + qk_rope_head_dim 64 with one shared KV
+ *     head, pool [tokens, 1, 576] (same page, section "The Investigation Leading to This
+ *     Message"); the value is the first 512 dims of the same row;
+ *   - the KV may stay in FP8 e4m3fn or NVFP4 and is dequantized inside the kernel
+ *     instead of casting the pool to BF16 (the cast is the bottleneck found on that
+ *     page; NVFP4 decode reads the packed format directly: NVFP4 article on aitop.news,
+ *     implementation item 3);
+ *   - NVFP4 = E2M1 values, one E4M3 scale per 16 values, one FP32 global scale (same
+ *     article, format section); the cache is filled by quantize-on-write (item 1).
+ *
+ * Layouts (row-major, contiguous):
+ *   q            bf16 bits  [batch, num_heads, 576]; dims 0-511 latent, 512-575 rope
+ *   FP8 pool     e4m3fn     [pool_tokens, 576]
+ *   BF16 pool    bf16 bits  [pool_tokens, 576]
+ *   NVFP4 pool   data       [pool_tokens, 288]  byte j = code(dim 2j) | code(dim 2j+1) << 4
+ *                scales     [pool_tokens, 36]   e4m3fn; scale k covers dims 16k .. 16k+15
+ *   kv_indptr    int32 [batch + 1]  page offsets of each request into kv_indices
+ *   kv_indices   int32 [kv_indptr[batch]]  physical page ids; token j of request b lives in
+ *                pool row kv_indices[kv_indptr[b] + j / page_size] * page_size + j % page_size
+ *   kv_lens      int32 [batch]  tokens per request
+ *   out          fp32 [batch, num_heads, 512]
+ *   lse          fp32 [batch, num_heads] natural-log sum of exp of the scaled scores; may be NULL
+ *
+ * Device-resident contents are checked in the kernels without faulting: a request whose
+ * length is negative, above max_kv_len or beyond its pages, or that names a page outside
+ * the pool, gets NaN in out and lse.  A request with kv_len 0 gets out = 0, lse = -inf.
+ */
+#ifndef MLAQ_H
+#define MLAQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLAQ_HEAD_DIM 576
+#define MLAQ_LATENT_DIM 512
+#define MLAQ_ROPE_DIM 64
+#define MLAQ_NVFP4_DATA_BYTES 288
+#define MLAQ_NVFP4_SCALE_BYTES 36
+#define MLAQ_MAX_SPLITS 1024
+#define MLAQ_MAX_KV_LEN (1 << 26)
+
+typedef enum {
+  MLAQ_OK = 0,
+  MLAQ_ERR_NULL = 1,        /* a required pointer is NULL */
+  MLAQ_ERR_SHAPE = 2,       /* a size is out of the supported range */
+  MLAQ_ERR_ALIGN = 3,       /* a pointer is not aligned as documented */
+  MLAQ_ERR_UNSUPPORTED = 4, /* format combination not implemented */
+  MLAQ_ERR_WORKSPACE = 5,   /* workspace smaller than mlaq_decode_workspace_bytes() */
+  MLAQ_ERR_LAUNCH = 6,      /* the HIP launch itself failed */
+  MLAQ_ERR_VALUE = 7        /* a scalar argument is not finite / not positive */
+} mlaq_status;
+
+typedef enum { MLAQ_BF16 = 0, MLAQ_FP8_E4M3 = 1, MLAQ_NVFP4 = 2, MLAQ_FP32 = 3 } mlaq_format;
+
+typedef struct {            /* (host) */
+  int32_t batch;            /* >= 0; 0 is a no-op */
+  int32_t num_heads;        /* multiple of 16, 16 .. 128 */
+  int32_t page_size;        /* 1 .. 1024 tokens per page */
+  int32_t max_kv_len;       /* host upper bound of kv_lens[] (split planning), 0 .. MLAQ_MAX_KV_LEN */
+  int64_t pool_tokens;      /* rows in the pool (> 0) */
+  int32_t num_splits;       /* KV chunks per request; 0 = choose automatically */
+  float sm_scale;           /* multiplies q . k before the softmax; finite */
+} mlaq_decode_params;
+
+/* (host) Splits the decode will use for these parameters (resolves num_splits = 0), or 0 if
+ * the parameters are invalid.  Depends on host arguments only. */
+int32_t mlaq_decode_num_splits(const mlaq_decode_params* p);
+
+/* (host) Workspace bytes a decode with these parameters needs (0 when it needs none,
+ * which is the case for a single split), or SIZE_MAX if the parameters are invalid.
+ * The workspace holds one fp32 partial output plus running max and sum per
+ * (request, split, 16-head group); it must be 256-byte aligned. */
+size_t mlaq_decode_workspace_bytes(const mlaq_decode_params* p);
+
+/* Decode over an FP8 e4m3fn pool.  kv_scale (> 0, finite) is the per-tensor dequant
+ * multiplier: k = e4m3(code) * kv_scale.  Alignment: q, kv, out 16 B; lse 4 B. */
+mlaq_status mla_decode_fp8(const mlaq_decode_params* p, const uint16_t* q, const uint8_t* kv, float kv_scale,
+                           const int32_t* kv_indptr, const int32_t* kv_indices, const int32_t* kv_lens,
+                           float* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Decode over an NVFP4 pool: k = e2m1(code) * e4m3(block scale) * global_scale.
+ * Alignment: q, kv_data, out 16 B; kv_scales 4 B; lse 4 B. */
+mlaq_status mla_decode_nvfp4(const mlaq_decode_params* p, const uint16_t* q, const uint8_t* kv_data,
+                             const uint8_t* kv_scales, float global_scale, const int32_t* kv_indptr,
+                             const int32_t* kv_indices, const int32_t* kv_lens, float* out, float* lse,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Decode over a BF16 pool (the comparison path that first casts an FP8 pool to BF16,
+ * as the pages' server did, and a cross-check of the quantized paths). */
+mlaq_status mla_decode_bf16(const mlaq_decode_params* p, const uint16_t* q, const uint16_t* kv,
+                            const int32_t* kv_indptr, const int32_t* kv_indices, const int32_t* kv_lens,
+                            float* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* NVFP4 quantize-on-write (NVFP4 article, implementation item 1): each source row of 576
+ * values becomes 36 blocks of 16, written to pool row slot_mapping[t] (rows with a
+ * negative slot are skipped; a slot >= pool_tokens is skipped too and not written).
+ * Per block, in IEEE fp32 with round-to-nearest-even: scale byte = e4m3(sat) of
+ * (amax / 6) / global_scale; codes = e2m1(sat) of x / (e4m3(scale) * global_scale);
+ * a NaN in the block gives scale 0x7F and zero codes; a zero divisor gives zero codes.
+ * src: MLAQ_FP8_E4M3 bytes (x = e4m3 * src_scale) or MLAQ_BF16 bits, [num_tokens, 576],
+ * 16-B aligned.  kv_data 16-B aligned, kv_scales 4-B aligned. */
+mlaq_status kv_quantize_nvfp4(const void* src, mlaq_format src_format, float src_scale, int64_t num_tokens,
+                              const int64_t* slot_mapping, uint8_t* kv_data, uint8_t* kv_scales,
+                              int64_t pool_tokens, float global_scale, hipStream_t stream);
+
+/* Dequantize pool rows into a dense buffer dst [num_rows, 576].
+ * src_format MLAQ_FP8_E4M3: value = e4m3(code) * scale (kv_scales must be NULL);
+ * src_format MLAQ_NVFP4:    value = e2m1 * e4m3(block scale) * scale.
+ * The fp32 value is fl32(fl32(e2m1 * e4m3) * scale) (fl32(e4m3 * scale) for FP8);
+ * dst_format MLAQ_FP32 stores it, MLAQ_BF16 rounds it to nearest even, MLAQ_FP8_E4M3
+ * re-encodes it (nearest even, saturating at 448; NVFP4 source only).
+ * rows: int64 [num_rows] pool rows to read (each < pool_tokens, else the output row is
+ * NaN), or NULL for rows 0 .. num_rows-1.  kv_data and dst 16-B aligned. */
+mlaq_status kv_dequantize(mlaq_format src_format, const uint8_t* kv_data, const uint8_t* kv_scales, float scale,
+                          const int64_t* rows, int64_t num_rows, int64_t pool_tokens, mlaq_format dst_format,
+                          void* dst, hipStream_t stream);
+
+/* (host) Profiling hook for callers that time the kernels themselves.  Registers up to three
+ * HIP events (hipEvent_t, or NULL) for the NEXT decode call made on this thread: it records
+ * `before_split` on its stream before the split-KV kernel, `after_split` after it (before
+ * the merge kernel, if any) and `after_merge` after the last kernel; then the registration
+ * is cleared.  The events are owned by the caller. */
+mlaq_status mlaq_set_profile_events(hipEvent_t before_split, hipEvent_t after_split, hipEvent_t after_merge);
+
+/* (host) Message for the last non-OK status returned on this thread ("" if none). */
+const char* mlaq_last_error(void);
+
+/* (host) Library version string. */
+const char* mlaq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLAQ_H */

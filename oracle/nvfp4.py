@@ -124,6 +124,9 @@ def _lib():
         _LIB.oracle_e2m1_encode_f32.restype = ctypes.c_int
         _LIB.oracle_e4m3_encode_f32.argtypes = [ctypes.c_float]
         _LIB.oracle_e4m3_encode_f32.restype = ctypes.c_int
+        _LIB.oracle_e4m3_encode_array.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+        _LIB.oracle_nvfp4_dequant_f32_rows.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                                       ctypes.c_float, ctypes.c_void_p]
     return _LIB
 
 
@@ -164,6 +167,24 @@ def quantize_fp8_rows(codes: np.ndarray, src_scale: float, g: float) -> tuple[np
 
 def quantize_bf16_rows(bits: np.ndarray, g: float) -> tuple[np.ndarray, np.ndarray]:
     return quantize_rows(bf16_rows_to_f32(bits), g)
+
+
+def e4m3_encode_array(x: np.ndarray) -> np.ndarray:
+    """Element-wise e4m3fn encode (nearest, ties to even, saturating) of an fp32 array."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint8)
+    _lib().oracle_e4m3_encode_array(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def dequant_nvfp4_f32(data: np.ndarray, scales: np.ndarray, g: float) -> np.ndarray:
+    """fp32 dequantized rows: fl32(fl32(e2m1 * e4m3) * g) (the product itself is exact)."""
+    data = np.ascontiguousarray(data, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    n = data.shape[0]
+    out = np.empty((n, ROW_DIMS), dtype=np.float32)
+    _lib().oracle_nvfp4_dequant_f32_rows(_ptr(data), _ptr(scales), n, g, _ptr(out))
+    return out
 
 
 def e2m1_encode_c(y: float) -> int:

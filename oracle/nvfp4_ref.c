@@ -124,3 +124,23 @@ void oracle_bf16_rows_to_f32(const uint16_t* src, int64_t n, float* out) {
     memcpy(&out[i], &b, 4);
   }
 }
+
+/* e4m3 encode of an array (nearest, ties to even, saturating; NaN -> 0x7F) */
+void oracle_e4m3_encode_array(const float* x, int64_t n, uint8_t* out) {
+  init_grids();
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = (uint8_t)oracle_e4m3_encode_f32(x[i]);
+}
+
+/* NVFP4 rows -> fp32 values fl32(fl32(e2m1 * e4m3) * g) */
+void oracle_nvfp4_dequant_f32_rows(const uint8_t* data, const uint8_t* scales, int64_t rows, float g, float* out) {
+  init_grids();
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r)
+    for (int d = 0; d < ROW; ++d) {
+      uint8_t byte = data[r * (ROW / 2) + d / 2];
+      int code = (d % 2) ? (byte >> 4) : (byte & 0xF);
+      float prod = (float)e2m1_value(code) * (float)e4m3_value(scales[r * (ROW / BLOCK) + d / BLOCK]);
+      out[r * ROW + d] = prod * g;
+    }
+}

@@ -1,0 +1,185 @@
+"""Python binding of libmlaq (paged MLA decode over FP8 / NVFP4 latent KV on MI355X).
+
+Argument marshalling only: every step of decode, quantize-on-write and dequantization
+runs in the HIP kernels of libmlaq.so, called through its C ABI (include/mlaq.h).
+PyTorch provides device memory and the current stream.  Importing this package fails
+loudly when the built library is missing; there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmlaq.so")
+
+MLAQ_BF16, MLAQ_FP8_E4M3, MLAQ_NVFP4, MLAQ_FP32 = 0, 1, 2, 3
+HEAD_DIM, LATENT_DIM, ROPE_DIM = 576, 512, 64
+NVFP4_DATA_BYTES, NVFP4_SCALE_BYTES = 288, 36
+STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_ALIGN", 4: "ERR_UNSUPPORTED", 5: "ERR_WORKSPACE",
+          6: "ERR_LAUNCH", 7: "ERR_VALUE"}
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m quantized_kv_paged_amd.build` "
+                      "(or __graft_entry__.build()); there is no fallback implementation")
+
+
+class DecodeParams(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("max_kv_len", ctypes.c_int32), ("pool_tokens", ctypes.c_int64), ("num_splits", ctypes.c_int32),
+                ("sm_scale", ctypes.c_float)]
+
+
+_lib = ctypes.CDLL(LIB_PATH)
+_vp, _i64, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+_pp = ctypes.POINTER(DecodeParams)
+_SIGS = {
+    "mlaq_decode_num_splits": ([_pp], _i32),
+    "mlaq_decode_workspace_bytes": ([_pp], _sz),
+    "mla_decode_fp8": ([_pp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "mla_decode_nvfp4": ([_pp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "mla_decode_bf16": ([_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "kv_quantize_nvfp4": ([_vp, ctypes.c_int, _f32, _i64, _vp, _vp, _vp, _i64, _f32, _vp], ctypes.c_int),
+    "kv_dequantize": ([ctypes.c_int, _vp, _vp, _f32, _vp, _i64, _i64, ctypes.c_int, _vp, _vp], ctypes.c_int),
+    "mlaq_set_profile_events": ([_vp, _vp, _vp], ctypes.c_int),
+    "mlaq_last_error": ([], ctypes.c_char_p),
+    "mlaq_version": ([], ctypes.c_char_p),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes, _fn.restype = _args, _res
+
+EXPORTS = tuple(_SIGS)
+
+
+class MlaqError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise MlaqError(status, _lib.mlaq_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream
+    return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+
+
+def mlaq_set_profile_events(before_split, after_split, after_merge) -> None:
+    """Raw hipEvent_t handles (ints or None) recorded by the next decode call on this thread."""
+    _check(_lib.mlaq_set_profile_events(before_split, after_split, after_merge))
+
+
+def version() -> str:
+    return _lib.mlaq_version().decode()
+
+
+def last_error() -> str:
+    return _lib.mlaq_last_error().decode()
+
+
+def decode_params(batch, num_heads, page_size, max_kv_len, pool_tokens, sm_scale, num_splits=0) -> DecodeParams:
+    return DecodeParams(batch, num_heads, page_size, max_kv_len, pool_tokens, num_splits, sm_scale)
+
+
+def mlaq_decode_num_splits(p: DecodeParams) -> int:
+    return _lib.mlaq_decode_num_splits(ctypes.byref(p))
+
+
+def mlaq_decode_workspace_bytes(p: DecodeParams) -> int:
+    n = _lib.mlaq_decode_workspace_bytes(ctypes.byref(p))
+    if n == ctypes.c_size_t(-1).value:
+        raise MlaqError(2, last_error())
+    return n
+
+
+def alloc_workspace(p: DecodeParams, device="cuda") -> torch.Tensor | None:
+    n = mlaq_decode_workspace_bytes(p)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def _decode_outputs(q, out, lse, want_lse):
+    B, H = q.shape[0], q.shape[1]
+    if out is None:
+        out = torch.empty((B, H, LATENT_DIM), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    return out, lse
+
+
+def _params_for(q, page_size, max_kv_len, pool_tokens, sm_scale, num_splits):
+    return decode_params(q.shape[0], q.shape[1], page_size, max_kv_len, pool_tokens, sm_scale, num_splits)
+
+
+def mla_decode_fp8(q, kv, kv_scale, kv_indptr, kv_indices, kv_lens, page_size, max_kv_len, sm_scale, *,
+                   num_splits=0, out=None, lse=None, want_lse=True, workspace=None, stream=None):
+    """q: bf16 [B, H, 576]; kv: uint8 e4m3fn [pool, 576]; page table int32 tensors; returns (out, lse)."""
+    p = _params_for(q, page_size, max_kv_len, kv.shape[0], sm_scale, num_splits)
+    out, lse = _decode_outputs(q, out, lse, want_lse)
+    if workspace is None:
+        workspace = alloc_workspace(p, q.device)
+    _check(_lib.mla_decode_fp8(ctypes.byref(p), _ptr(q), _ptr(kv), kv_scale, _ptr(kv_indptr), _ptr(kv_indices),
+                               _ptr(kv_lens), _ptr(out), _ptr(lse), _ptr(workspace),
+                               0 if workspace is None else workspace.numel(), _stream(stream)))
+    return out, lse
+
+
+def mla_decode_nvfp4(q, kv_data, kv_scales, global_scale, kv_indptr, kv_indices, kv_lens, page_size, max_kv_len,
+                     sm_scale, *, num_splits=0, out=None, lse=None, want_lse=True, workspace=None, stream=None):
+    """q: bf16 [B, H, 576]; kv_data uint8 [pool, 288]; kv_scales uint8 [pool, 36]; returns (out, lse)."""
+    p = _params_for(q, page_size, max_kv_len, kv_data.shape[0], sm_scale, num_splits)
+    out, lse = _decode_outputs(q, out, lse, want_lse)
+    if workspace is None:
+        workspace = alloc_workspace(p, q.device)
+    _check(_lib.mla_decode_nvfp4(ctypes.byref(p), _ptr(q), _ptr(kv_data), _ptr(kv_scales), global_scale,
+                                 _ptr(kv_indptr), _ptr(kv_indices), _ptr(kv_lens), _ptr(out), _ptr(lse),
+                                 _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream)))
+    return out, lse
+
+
+def mla_decode_bf16(q, kv, kv_indptr, kv_indices, kv_lens, page_size, max_kv_len, sm_scale, *,
+                    num_splits=0, out=None, lse=None, want_lse=True, workspace=None, stream=None):
+    """q: bf16 [B, H, 576]; kv: bf16 [pool, 576]; returns (out, lse)."""
+    p = _params_for(q, page_size, max_kv_len, kv.shape[0], sm_scale, num_splits)
+    out, lse = _decode_outputs(q, out, lse, want_lse)
+    if workspace is None:
+        workspace = alloc_workspace(p, q.device)
+    _check(_lib.mla_decode_bf16(ctypes.byref(p), _ptr(q), _ptr(kv), _ptr(kv_indptr), _ptr(kv_indices),
+                                _ptr(kv_lens), _ptr(out), _ptr(lse), _ptr(workspace),
+                                0 if workspace is None else workspace.numel(), _stream(stream)))
+    return out, lse
+
+
+def kv_quantize_nvfp4(src, src_format, src_scale, slot_mapping, kv_data, kv_scales, global_scale, *, stream=None):
+    """src: uint8 e4m3fn or bf16 [n, 576]; slot_mapping int64 [n]; writes kv_data / kv_scales rows in place."""
+    n = src.shape[0]
+    _check(_lib.kv_quantize_nvfp4(_ptr(src), src_format, src_scale, n, _ptr(slot_mapping), _ptr(kv_data),
+                                  _ptr(kv_scales), kv_data.shape[0], global_scale, _stream(stream)))
+
+
+def kv_dequantize(src_format, kv_data, kv_scales, scale, dst_format, *, rows=None, num_rows=None, dst=None,
+                  stream=None):
+    """Dequantize pool rows (all rows when rows is None) into dst [num_rows, 576]."""
+    if num_rows is None:
+        num_rows = rows.shape[0] if rows is not None else kv_data.shape[0]
+    if dst is None:
+        dt = {MLAQ_BF16: torch.bfloat16, MLAQ_FP32: torch.float32, MLAQ_FP8_E4M3: torch.uint8}[dst_format]
+        dst = torch.empty((num_rows, HEAD_DIM), dtype=dt, device=kv_data.device)
+    _check(_lib.kv_dequantize(src_format, _ptr(kv_data), _ptr(kv_scales), scale, _ptr(rows), num_rows,
+                              kv_data.shape[0], dst_format, _ptr(dst), _stream(stream)))
+    return dst
+
+
+__all__ = ["mla_decode_fp8", "mla_decode_nvfp4", "mla_decode_bf16", "kv_quantize_nvfp4", "kv_dequantize",
+           "mlaq_decode_num_splits", "mlaq_decode_workspace_bytes", "decode_params", "alloc_workspace",
+           "MlaqError", "version", "last_error", "EXPORTS", "LIB_PATH"]

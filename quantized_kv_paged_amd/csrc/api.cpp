@@ -1,0 +1,251 @@
+// Host side of the mlaq C ABI: argument validation, split planning, workspace layout and
+// kernel launches.  Nothing here touches device memory or synchronises.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <limits>
+#include <string>
+
+#include "../../include/mlaq.h"
+#include "mlaq_kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+thread_local mlaq::ProfileEvents g_events;
+
+mlaq_status fail(mlaq_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
+
+constexpr int kTileTokens = 64;         // tokens per decode tile
+constexpr int kResidentSlots = 2 * 256; // resident decode workgroups on one MI355X (256 CUs x 2)
+
+// Split planning.  Every workgroup processes one (request, chunk, 16-head group); with all
+// requests at the host-known bound, workgroups run in "rounds" of kResidentSlots.  The cost
+// (in tile-times) is rounds * (tiles per chunk + fixed per-workgroup cost) plus the partial
+// write + merge read, and the smallest-cost split count is taken (ties -> fewer splits).
+int plan_splits(int batch, int head_groups, int max_kv_len) {
+  const int tiles = (max_kv_len + kTileTokens - 1) / kTileTokens;
+  if (tiles <= 1 || batch <= 0) return 1;
+  const double fixed = 0.5, merge = 0.5;
+  int best = 1;
+  double best_cost = std::numeric_limits<double>::infinity();
+  const int smax = tiles < MLAQ_MAX_SPLITS ? tiles : MLAQ_MAX_SPLITS;
+  for (int s = 1; s <= smax; ++s) {
+    const double wgs = (double)batch * head_groups * s;
+    const double rounds = std::ceil(wgs / kResidentSlots);
+    const double per = std::ceil((double)tiles / s);
+    const double cost = rounds * (per + fixed) + (s > 1 ? merge * wgs / kResidentSlots : 0.0);
+    if (cost < best_cost - 1e-9) { best_cost = cost; best = s; }
+  }
+  return best;
+}
+
+mlaq_status check_params(const mlaq_decode_params* p) {
+  if (!p) return fail(MLAQ_ERR_NULL, "params is NULL");
+  if (p->batch < 0 || p->batch > 65535) return fail(MLAQ_ERR_SHAPE, "batch %d not in [0, 65535]", p->batch);
+  if (p->num_heads < 16 || p->num_heads > 128 || p->num_heads % 16)
+    return fail(MLAQ_ERR_SHAPE, "num_heads %d: must be a multiple of 16 in [16, 128]", p->num_heads);
+  if (p->page_size < 1 || p->page_size > 1024) return fail(MLAQ_ERR_SHAPE, "page_size %d not in [1, 1024]", p->page_size);
+  if (p->max_kv_len < 0 || p->max_kv_len > MLAQ_MAX_KV_LEN)
+    return fail(MLAQ_ERR_SHAPE, "max_kv_len %d not in [0, %d]", p->max_kv_len, MLAQ_MAX_KV_LEN);
+  if (p->pool_tokens <= 0 || p->pool_tokens > ((int64_t)1 << 40))
+    return fail(MLAQ_ERR_SHAPE, "pool_tokens %lld out of range", (long long)p->pool_tokens);
+  if (p->num_splits < 0 || p->num_splits > MLAQ_MAX_SPLITS)
+    return fail(MLAQ_ERR_SHAPE, "num_splits %d not in [0, %d]", p->num_splits, MLAQ_MAX_SPLITS);
+  if (!std::isfinite(p->sm_scale)) return fail(MLAQ_ERR_VALUE, "sm_scale is not finite");
+  return MLAQ_OK;
+}
+
+int resolve_splits(const mlaq_decode_params* p) {
+  return p->num_splits > 0 ? p->num_splits : plan_splits(p->batch, p->num_heads / 16, p->max_kv_len);
+}
+
+size_t workspace_for(const mlaq_decode_params* p, int splits) {
+  if (splits <= 1) return 0;
+  const size_t slots = (size_t)p->batch * (size_t)splits * (size_t)(p->num_heads / 16);
+  const size_t bytes = slots * (16 * 512 * sizeof(float)) + slots * 32 * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+mlaq_status decode_common(int fmt, const mlaq_decode_params* p, const uint16_t* q, const void* kv,
+                          const uint8_t* kv_scales, float scale, const int32_t* kv_indptr,
+                          const int32_t* kv_indices, const int32_t* kv_lens, float* out, float* lse,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  mlaq_status st = check_params(p);
+  if (st != MLAQ_OK) return st;
+  if (p->batch == 0) return MLAQ_OK;
+  if (!q || !kv || !kv_indptr || !kv_indices || !kv_lens || !out)
+    return fail(MLAQ_ERR_NULL, "a required pointer (q, kv, kv_indptr, kv_indices, kv_lens, out) is NULL");
+  if (fmt == mlaq::FMT_NVFP4 && !kv_scales) return fail(MLAQ_ERR_NULL, "kv_scales is NULL");
+  if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(out, 16))
+    return fail(MLAQ_ERR_ALIGN, "q, kv and out must be 16-byte aligned");
+  if (fmt == mlaq::FMT_NVFP4 && !aligned(kv_scales, 4)) return fail(MLAQ_ERR_ALIGN, "kv_scales must be 4-byte aligned");
+  if (lse && !aligned(lse, 4)) return fail(MLAQ_ERR_ALIGN, "lse must be 4-byte aligned");
+  if (!aligned(kv_indptr, 4) || !aligned(kv_indices, 4) || !aligned(kv_lens, 4))
+    return fail(MLAQ_ERR_ALIGN, "kv_indptr, kv_indices and kv_lens must be 4-byte aligned");
+  if (fmt != mlaq::FMT_BF16 && !finite_pos(scale))
+    return fail(MLAQ_ERR_VALUE, "the KV scale must be finite and > 0 (got %g)", (double)scale);
+  const int splits = resolve_splits(p);
+  const size_t need = workspace_for(p, splits);
+  if (need > 0) {
+    if (!workspace) return fail(MLAQ_ERR_NULL, "workspace is NULL but %zu bytes are needed", need);
+    if (workspace_bytes < need)
+      return fail(MLAQ_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+    if (!aligned(workspace, 256)) return fail(MLAQ_ERR_ALIGN, "workspace must be 256-byte aligned");
+  }
+  const int tiles = (p->max_kv_len + kTileTokens - 1) / kTileTokens;
+  const int per = (tiles + splits - 1) / splits;
+
+  mlaq::DecodeArgs a;
+  a.q = q;
+  a.kv = static_cast<const uint8_t*>(kv);
+  a.kv_scales = kv_scales;
+  a.kv_indptr = kv_indptr;
+  a.kv_indices = kv_indices;
+  a.kv_lens = kv_lens;
+  a.out = out;
+  a.lse = lse;
+  const size_t slots = (size_t)p->batch * splits * (p->num_heads / 16);
+  a.part_o = need ? static_cast<float*>(workspace) : nullptr;
+  a.part_ml = need ? static_cast<float*>(workspace) + slots * 16 * 512 : nullptr;
+  a.pool_tokens = p->pool_tokens;
+  a.batch = p->batch;
+  a.num_heads = p->num_heads;
+  a.page_size = p->page_size;
+  a.max_kv_len = p->max_kv_len;
+  a.num_splits = splits;
+  a.chunk_tokens = (per > 0 ? per : 1) * kTileTokens;
+  const float s = fmt == mlaq::FMT_BF16 ? 1.0f : scale;
+  a.score_scale = p->sm_scale * s * 1.4426950408889634f;
+  a.out_scale = s;
+  const mlaq::ProfileEvents ev = g_events;
+  g_events = mlaq::ProfileEvents();
+  hipError_t e = mlaq::launch_decode(fmt, a, stream, ev);
+  if (e != hipSuccess) return fail(MLAQ_ERR_LAUNCH, "decode launch failed: %s", hipGetErrorString(e));
+  return MLAQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mlaq_last_error(void) { return g_err.c_str(); }
+
+const char* mlaq_version(void) { return "mlaq 0.1 gfx950"; }
+
+mlaq_status mlaq_set_profile_events(hipEvent_t before_split, hipEvent_t after_split, hipEvent_t after_merge) {
+  g_events.before_split = before_split;
+  g_events.after_split = after_split;
+  g_events.after_merge = after_merge;
+  return MLAQ_OK;
+}
+
+int32_t mlaq_decode_num_splits(const mlaq_decode_params* p) {
+  if (check_params(p) != MLAQ_OK) return 0;
+  return resolve_splits(p);
+}
+
+size_t mlaq_decode_workspace_bytes(const mlaq_decode_params* p) {
+  if (check_params(p) != MLAQ_OK) return SIZE_MAX;
+  return workspace_for(p, resolve_splits(p));
+}
+
+mlaq_status mla_decode_fp8(const mlaq_decode_params* p, const uint16_t* q, const uint8_t* kv, float kv_scale,
+                           const int32_t* kv_indptr, const int32_t* kv_indices, const int32_t* kv_lens, float* out,
+                           float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return decode_common(mlaq::FMT_FP8, p, q, kv, nullptr, kv_scale, kv_indptr, kv_indices, kv_lens, out, lse,
+                       workspace, workspace_bytes, stream);
+}
+
+mlaq_status mla_decode_nvfp4(const mlaq_decode_params* p, const uint16_t* q, const uint8_t* kv_data,
+                             const uint8_t* kv_scales, float global_scale, const int32_t* kv_indptr,
+                             const int32_t* kv_indices, const int32_t* kv_lens, float* out, float* lse,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return decode_common(mlaq::FMT_NVFP4, p, q, kv_data, kv_scales, global_scale, kv_indptr, kv_indices, kv_lens,
+                       out, lse, workspace, workspace_bytes, stream);
+}
+
+mlaq_status mla_decode_bf16(const mlaq_decode_params* p, const uint16_t* q, const uint16_t* kv,
+                            const int32_t* kv_indptr, const int32_t* kv_indices, const int32_t* kv_lens, float* out,
+                            float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return decode_common(mlaq::FMT_BF16, p, q, kv, nullptr, 1.0f, kv_indptr, kv_indices, kv_lens, out, lse,
+                       workspace, workspace_bytes, stream);
+}
+
+mlaq_status kv_quantize_nvfp4(const void* src, mlaq_format src_format, float src_scale, int64_t num_tokens,
+                              const int64_t* slot_mapping, uint8_t* kv_data, uint8_t* kv_scales, int64_t pool_tokens,
+                              float global_scale, hipStream_t stream) {
+  if (src_format != MLAQ_FP8_E4M3 && src_format != MLAQ_BF16)
+    return fail(MLAQ_ERR_UNSUPPORTED, "kv_quantize_nvfp4: source format %d is not FP8_E4M3 or BF16", (int)src_format);
+  if (num_tokens < 0 || num_tokens > ((int64_t)1 << 32))
+    return fail(MLAQ_ERR_SHAPE, "num_tokens %lld out of range", (long long)num_tokens);
+  if (pool_tokens <= 0 || pool_tokens > ((int64_t)1 << 40))
+    return fail(MLAQ_ERR_SHAPE, "pool_tokens %lld out of range", (long long)pool_tokens);
+  if (!finite_pos(global_scale)) return fail(MLAQ_ERR_VALUE, "global_scale must be finite and > 0");
+  if (src_format == MLAQ_FP8_E4M3 && !finite_pos(src_scale)) return fail(MLAQ_ERR_VALUE, "src_scale must be finite and > 0");
+  if (num_tokens == 0) return MLAQ_OK;
+  if (!src || !slot_mapping || !kv_data || !kv_scales) return fail(MLAQ_ERR_NULL, "a required pointer is NULL");
+  if (!aligned(src, 16) || !aligned(kv_data, 16) || !aligned(kv_scales, 4) || !aligned(slot_mapping, 8))
+    return fail(MLAQ_ERR_ALIGN, "src and kv_data need 16-byte, kv_scales 4-byte, slot_mapping 8-byte alignment");
+  mlaq::QuantArgs a;
+  a.src = src;
+  a.slots = slot_mapping;
+  a.kv_data = kv_data;
+  a.kv_scales = kv_scales;
+  a.num_tokens = num_tokens;
+  a.pool_tokens = pool_tokens;
+  a.src_scale = src_scale;
+  a.global_scale = global_scale;
+  a.src_bf16 = src_format == MLAQ_BF16;
+  hipError_t e = mlaq::launch_quantize_nvfp4(a, stream);
+  if (e != hipSuccess) return fail(MLAQ_ERR_LAUNCH, "quantize launch failed: %s", hipGetErrorString(e));
+  return MLAQ_OK;
+}
+
+mlaq_status kv_dequantize(mlaq_format src_format, const uint8_t* kv_data, const uint8_t* kv_scales, float scale,
+                          const int64_t* rows, int64_t num_rows, int64_t pool_tokens, mlaq_format dst_format, void* dst,
+                          hipStream_t stream) {
+  if (src_format != MLAQ_FP8_E4M3 && src_format != MLAQ_NVFP4)
+    return fail(MLAQ_ERR_UNSUPPORTED, "kv_dequantize: source format %d is not FP8_E4M3 or NVFP4", (int)src_format);
+  if (dst_format != MLAQ_BF16 && dst_format != MLAQ_FP32 && dst_format != MLAQ_FP8_E4M3)
+    return fail(MLAQ_ERR_UNSUPPORTED, "kv_dequantize: destination format %d not supported", (int)dst_format);
+  if (dst_format == MLAQ_FP8_E4M3 && src_format != MLAQ_NVFP4)
+    return fail(MLAQ_ERR_UNSUPPORTED, "kv_dequantize: FP8 destination needs an NVFP4 source");
+  if (src_format == MLAQ_FP8_E4M3 && kv_scales)
+    return fail(MLAQ_ERR_UNSUPPORTED, "kv_dequantize: kv_scales must be NULL for an FP8 source");
+  if (num_rows < 0 || num_rows > ((int64_t)1 << 36)) return fail(MLAQ_ERR_SHAPE, "num_rows out of range");
+  if (pool_tokens <= 0 || pool_tokens > ((int64_t)1 << 40)) return fail(MLAQ_ERR_SHAPE, "pool_tokens out of range");
+  if (!rows && num_rows > pool_tokens) return fail(MLAQ_ERR_SHAPE, "num_rows > pool_tokens with rows == NULL");
+  if (!finite_pos(scale)) return fail(MLAQ_ERR_VALUE, "scale must be finite and > 0");
+  if (num_rows == 0) return MLAQ_OK;
+  if (!kv_data || !dst || (src_format == MLAQ_NVFP4 && !kv_scales)) return fail(MLAQ_ERR_NULL, "a required pointer is NULL");
+  if (!aligned(kv_data, 16) || !aligned(dst, 16) || (rows && !aligned(rows, 8)))
+    return fail(MLAQ_ERR_ALIGN, "kv_data and dst need 16-byte alignment, rows 8-byte");
+  mlaq::DequantArgs a;
+  a.kv_data = kv_data;
+  a.kv_scales = kv_scales;
+  a.rows = rows;
+  a.dst = dst;
+  a.num_rows = num_rows;
+  a.pool_tokens = pool_tokens;
+  a.scale = scale;
+  a.src_nvfp4 = src_format == MLAQ_NVFP4;
+  a.dst_format = (int)dst_format;
+  hipError_t e = mlaq::launch_dequantize(a, stream);
+  if (e != hipSuccess) return fail(MLAQ_ERR_LAUNCH, "dequantize launch failed: %s", hipGetErrorString(e));
+  return MLAQ_OK;
+}
+
+}  // extern "C"

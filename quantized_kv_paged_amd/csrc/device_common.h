@@ -1,0 +1,99 @@
+// Device helpers shared by the mlaq kernels (gfx950 / CDNA4).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mlaq {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __fp16 fp16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// 4-byte-aligned vector for loads from rows whose base is only dword aligned
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+
+constexpr int kD = 576;       // latent row: kv_lora_rank 512 + rope 64
+constexpr int kDV = 512;      // value dims (latent part)
+constexpr int kNvData = 288;  // NVFP4 code bytes per row
+constexpr int kNvScale = 36;  // NVFP4 scale bytes per row
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// Two e4m3fn bytes (low or high 16 bits of w) -> two fp16, exact (every e4m3fn value is an
+// fp16 value).  The scale operand of the gfx950 scaled conversion only applies the
+// exponent of its argument, so it is kept at 1.0 here and scales are applied separately.
+template <bool HI>
+__device__ __forceinline__ f16x2 fp8x2_to_f16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
+}
+
+// Two E2M1 nibbles (byte SEL of w; low nibble first) -> two fp16, exact.
+template <int SEL>
+__device__ __forceinline__ f16x2 fp4x2_to_f16(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
+}
+
+// Two e4m3fn bytes -> two fp32, exact.
+template <bool HI>
+__device__ __forceinline__ f32x2 fp8x2_to_f32(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposed 64-bit LDS read of 16-bit elements.  Within each group of 16 lanes, lane j
+// receives, as element c, 16-bit component (j % 4) of the 8 bytes addressed by lane
+// 4c + j / 4 of the same group (checked on gfx950 with an in-bounds index pattern).
+__device__ __forceinline__ i16x4 lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(reinterpret_cast<uintptr_t>(p)));
+}
+
+// fp32 -> bf16 bits, round to nearest even, quiet NaN kept.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+  uint32_t u = f2u(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// fp32 -> e4m3fn byte: round to nearest even, saturate to +-448, NaN -> 0x7F, sign kept.
+__device__ __forceinline__ uint32_t f32_to_e4m3_rne_sat(float x) {
+  uint32_t u = f2u(x);
+  uint32_t sign = (u >> 24) & 0x80u;
+  float a = __builtin_fabsf(x);
+  if (a != a) return 0x7Fu;
+  if (a >= 448.0f) return sign | 0x7Eu;
+  if (a < 0.015625f) {                       // below 2^-6: subnormal grid of step 2^-9
+    return sign | (uint32_t)__builtin_rintf(a * 512.0f);
+  }
+  int e = (int)((f2u(a) >> 23) & 0xff) - 127;                 // -6 .. 8
+  float q = __builtin_rintf(a * u2f((uint32_t)(127 + 3 - e) << 23));  // 8 .. 16
+  return sign | ((uint32_t)(e + 7) << 3) + ((uint32_t)q - 8u);
+}
+
+// fp32 -> E2M1 nibble: round to nearest even on {0,.5,1,1.5,2,3,4,6}, saturate, sign kept.
+// The code counts the grid midpoints below |y|; a midpoint whose upper neighbour has an
+// odd code is passed only strictly, so exact ties land on the even code.
+__device__ __forceinline__ uint32_t f32_to_e2m1_rne_sat(float y) {
+  float a = __builtin_fabsf(y);
+  uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) + (uint32_t)(a >= 1.75f) +
+               (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
+  return c | ((f2u(y) >> 28) & 0x8u);
+}
+
+}  // namespace mlaq

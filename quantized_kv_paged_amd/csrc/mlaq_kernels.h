@@ -1,0 +1,55 @@
+// Internal interface between the host-side C ABI (api.cpp) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mlaq {
+
+enum KvFormat { FMT_BF16 = 0, FMT_FP8 = 1, FMT_NVFP4 = 2 };
+
+struct DecodeArgs {
+  const uint16_t* q;          // bf16 [B, H, 576]
+  const uint8_t* kv;          // FP8 [pool, 576] | NVFP4 codes [pool, 288] | BF16 [pool, 576]
+  const uint8_t* kv_scales;   // NVFP4 [pool, 36]
+  const int32_t* kv_indptr;
+  const int32_t* kv_indices;
+  const int32_t* kv_lens;
+  float* out;                 // [B, H, 512]
+  float* lse;                 // [B, H] or null
+  float* part_o;              // [B, S, H/16, 16, 512]
+  float* part_ml;             // [B, S, H/16, 32]: m (16) then l (16)
+  int64_t pool_tokens;
+  int32_t batch, num_heads, page_size, max_kv_len, num_splits, chunk_tokens;
+  float score_scale;          // sm_scale * (kv scale or global scale) * log2(e)
+  float out_scale;            // kv scale or global scale
+};
+
+struct ProfileEvents {
+  hipEvent_t before_split = nullptr, after_split = nullptr, after_merge = nullptr;
+};
+hipError_t launch_decode(int fmt, const DecodeArgs& a, hipStream_t stream, const ProfileEvents& ev);
+
+struct QuantArgs {
+  const void* src;            // FP8 bytes or bf16 bits [n, 576]
+  const int64_t* slots;       // [n]
+  uint8_t* kv_data;           // [pool, 288]
+  uint8_t* kv_scales;         // [pool, 36]
+  int64_t num_tokens, pool_tokens;
+  float src_scale, global_scale;
+  int src_bf16;
+};
+hipError_t launch_quantize_nvfp4(const QuantArgs& a, hipStream_t stream);
+
+struct DequantArgs {
+  const uint8_t* kv_data;
+  const uint8_t* kv_scales;   // NVFP4 only
+  const int64_t* rows;        // or null
+  void* dst;
+  int64_t num_rows, pool_tokens;
+  float scale;
+  int src_nvfp4;              // 0: FP8 source, 1: NVFP4 source
+  int dst_format;             // 0 bf16, 1 fp8, 3 fp32 (mlaq_format values)
+};
+hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream);
+
+}  // namespace mlaq

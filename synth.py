@@ -183,23 +183,23 @@ def write_source_fp8(w: Workload) -> np.ndarray:
     return to_fp8_bytes(bf16_bits_to_fp32(to_bf16_bits(x)))
 
 
-def build_fp8_pool(w: Workload, pt: PageTable, threads: int = 8) -> np.ndarray:
+def build_fp8_pool(w: Workload, pt: PageTable, threads: int = 16) -> np.ndarray:
     """Whole FP8 pool [pool_tokens, 576] uint8 in host memory: request rows scattered by the
     page table, free pages filled from the filler stream, write pages zero."""
     pool = np.zeros((w.pool_tokens, D), dtype=np.uint8)
     P = w.page_size
 
-    def fill_request(b: int) -> None:
-        L = int(pt.kv_lens[b])
+    def fill_chunk(task) -> None:
+        b, c0 = task
+        n = min(CHUNK, int(pt.kv_lens[b]) - c0)
         pages = pt.kv_indices[pt.kv_indptr[b]:pt.kv_indptr[b + 1]]
-        for c0 in range(0, L, CHUNK):
-            n = min(CHUNK, L - c0)
-            rows = kv_fp8(w, b, c0, n)
-            j = np.arange(c0, c0 + n)
-            pool[pages[j // P].astype(np.int64) * P + j % P] = rows
+        rows = kv_fp8(w, b, c0, n)
+        j = np.arange(c0, c0 + n)
+        pool[pages[j // P].astype(np.int64) * P + j % P] = rows
 
+    tasks = [(b, c0) for b in range(w.batch) for c0 in range(0, int(pt.kv_lens[b]), CHUNK)]
     with ThreadPoolExecutor(threads) as ex:
-        list(ex.map(fill_request, range(w.batch)))
+        list(ex.map(fill_chunk, tasks))
         list(ex.map(lambda p: pool.__setitem__(slice(int(p) * P, int(p) * P + P), filler_fp8(w, int(p))),
                     pt.free_pages))
     return pool

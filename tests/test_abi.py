@@ -1,0 +1,129 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function include/mlaq.h
+declares, rejects bad arguments with the documented status before any launch, and plans
+splits / workspace on the host."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from conftest import ROOT
+
+qk = pytest.importorskip("quantized_kv_paged_amd")
+from quantized_kv_paged_amd import DecodeParams, MlaqError  # noqa: E402
+
+HEADER = os.path.join(ROOT, "include", "mlaq.h")
+ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_VALUE = 1, 2, 3, 4, 5, 7
+
+
+def _declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\**\s+\**([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_functions_are_exported():
+    names = _declared_functions()
+    assert {"mla_decode_fp8", "mla_decode_nvfp4", "kv_quantize_nvfp4", "kv_dequantize"} <= set(names)
+    lib = ctypes.CDLL(qk.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    nm = subprocess.run(["nm", "-D", "--defined-only", qk.LIB_PATH], capture_output=True, text=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}$", nm, flags=re.M), n
+    assert set(qk.EXPORTS) == set(names)
+
+
+def _p(**kw):
+    d = dict(batch=2, num_heads=16, page_size=64, max_kv_len=4096, pool_tokens=1 << 16, num_splits=0,
+             sm_scale=0.07)
+    d.update(kw)
+    return DecodeParams(d["batch"], d["num_heads"], d["page_size"], d["max_kv_len"], d["pool_tokens"],
+                        d["num_splits"], d["sm_scale"])
+
+
+FAKE = 1 << 20  # a 256-byte aligned fake device address; never dereferenced on these paths
+
+
+def _fp8(p, q=FAKE, kv=FAKE, scale=1.0, indptr=FAKE, indices=FAKE, lens=FAKE, out=FAKE, lse=FAKE, ws=FAKE,
+         ws_bytes=1 << 30):
+    return qk._lib.mla_decode_fp8(ctypes.byref(p), q, kv, scale, indptr, indices, lens, out, lse, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_heads=8), ERR_SHAPE), (dict(num_heads=24), ERR_SHAPE), (dict(num_heads=144), ERR_SHAPE),
+    (dict(page_size=0), ERR_SHAPE), (dict(page_size=2048), ERR_SHAPE), (dict(batch=-1), ERR_SHAPE),
+    (dict(batch=70000), ERR_SHAPE), (dict(max_kv_len=-5), ERR_SHAPE), (dict(pool_tokens=0), ERR_SHAPE),
+    (dict(num_splits=2000), ERR_SHAPE), (dict(sm_scale=float("nan")), ERR_VALUE),
+])
+def test_param_validation(kw, status):
+    assert _fp8(_p(**kw)) == status
+    assert qk.last_error() != ""
+
+
+def test_pointer_and_value_validation():
+    p = _p()
+    assert qk._lib.mla_decode_fp8(None, FAKE, FAKE, 1.0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == ERR_NULL
+    assert _fp8(p, q=None) == ERR_NULL
+    assert _fp8(p, kv=None) == ERR_NULL
+    assert _fp8(p, indices=None) == ERR_NULL
+    assert _fp8(p, out=None) == ERR_NULL
+    assert _fp8(p, q=FAKE + 8) == ERR_ALIGN
+    assert _fp8(p, kv=FAKE + 4) == ERR_ALIGN
+    assert _fp8(p, lens=FAKE + 2) == ERR_ALIGN
+    assert _fp8(p, scale=0.0) == ERR_VALUE
+    assert _fp8(p, scale=float("inf")) == ERR_VALUE
+    assert _fp8(p, ws=None) == ERR_NULL
+    need = qk.mlaq_decode_workspace_bytes(p)
+    assert need > 0
+    assert _fp8(p, ws_bytes=need - 1) == ERR_WORKSPACE
+    assert _fp8(p, ws=FAKE + 16) == ERR_ALIGN
+    assert "workspace" in qk.last_error()
+    assert _fp8(_p(batch=0)) == 0                       # empty batch is a no-op
+    st = qk._lib.mla_decode_nvfp4(ctypes.byref(p), FAKE, FAKE, None, 1.0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  1 << 30, None)
+    assert st == ERR_NULL
+    st = qk._lib.mla_decode_nvfp4(ctypes.byref(p), FAKE, FAKE, FAKE + 2, 1.0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  1 << 30, None)
+    assert st == ERR_ALIGN
+
+
+def test_quantize_and_dequantize_validation():
+    L = qk._lib
+    assert L.kv_quantize_nvfp4(FAKE, 3, 1.0, 8, FAKE, FAKE, FAKE, 64, 1.0, None) == ERR_UNSUPPORTED
+    assert L.kv_quantize_nvfp4(FAKE, 2, 1.0, 8, FAKE, FAKE, FAKE, 64, 1.0, None) == ERR_UNSUPPORTED
+    assert L.kv_quantize_nvfp4(FAKE, 1, 1.0, 8, FAKE, FAKE, FAKE, 64, 0.0, None) == ERR_VALUE
+    assert L.kv_quantize_nvfp4(FAKE, 1, float("nan"), 8, FAKE, FAKE, FAKE, 64, 1.0, None) == ERR_VALUE
+    assert L.kv_quantize_nvfp4(None, 1, 1.0, 8, FAKE, FAKE, FAKE, 64, 1.0, None) == ERR_NULL
+    assert L.kv_quantize_nvfp4(FAKE + 4, 1, 1.0, 8, FAKE, FAKE, FAKE, 64, 1.0, None) == ERR_ALIGN
+    assert L.kv_quantize_nvfp4(FAKE, 1, 1.0, -1, FAKE, FAKE, FAKE, 64, 1.0, None) == ERR_SHAPE
+    assert L.kv_quantize_nvfp4(FAKE, 1, 1.0, 0, None, None, None, 64, 1.0, None) == 0
+    assert L.kv_dequantize(0, FAKE, None, 1.0, None, 4, 64, 0, FAKE, None) == ERR_UNSUPPORTED
+    assert L.kv_dequantize(1, FAKE, None, 1.0, None, 4, 64, 1, FAKE, None) == ERR_UNSUPPORTED  # FP8 -> FP8
+    assert L.kv_dequantize(1, FAKE, FAKE, 1.0, None, 4, 64, 0, FAKE, None) == ERR_UNSUPPORTED  # scales w/ FP8
+    assert L.kv_dequantize(2, FAKE, None, 1.0, None, 4, 64, 0, FAKE, None) == ERR_NULL
+    assert L.kv_dequantize(2, FAKE, FAKE, -1.0, None, 4, 64, 0, FAKE, None) == ERR_VALUE
+    assert L.kv_dequantize(2, FAKE, FAKE, 1.0, None, 65, 64, 0, FAKE, None) == ERR_SHAPE
+    assert L.kv_dequantize(2, FAKE, FAKE, 1.0, None, 4, 64, 0, FAKE + 8, None) == ERR_ALIGN
+    with pytest.raises(MlaqError) as e:
+        qk._check(L.kv_dequantize(2, FAKE, FAKE, 1.0, None, 65, 64, 0, FAKE, None))
+    assert e.value.status == ERR_SHAPE and "num_rows" in str(e.value)
+
+
+def test_split_planning_and_workspace():
+    import synth
+    expect = {"tiny_fp8": 8, "fp8_32k": 64, "nvfp4_32k": 11, "nvfp4_160k": 51, "nvfp4_1m": 256}
+    for name, w in synth.WORKLOADS.items():
+        p = _p(batch=w.batch, num_heads=w.heads, page_size=w.page_size, max_kv_len=w.kv_len,
+               pool_tokens=w.pool_tokens)
+        s = qk.mlaq_decode_num_splits(p)
+        assert s == expect[name], (name, s)
+        ws = qk.mlaq_decode_workspace_bytes(p)
+        slots = w.batch * s * (w.heads // 16)
+        assert ws == ((slots * (16 * 512 * 4 + 32 * 4) + 255) // 256) * 256
+    assert qk.mlaq_decode_num_splits(_p(max_kv_len=64)) == 1
+    assert qk.mlaq_decode_workspace_bytes(_p(max_kv_len=64)) == 0
+    assert qk.mlaq_decode_num_splits(_p(num_splits=7)) == 7
+    assert qk.mlaq_decode_num_splits(_p(num_heads=20)) == 0
+    with pytest.raises(MlaqError):
+        qk.mlaq_decode_workspace_bytes(_p(num_heads=20))

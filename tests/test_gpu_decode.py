@@ -1,0 +1,170 @@
+"""GPU parity of the decode kernels against the fp64 oracle, through the C ABI.
+
+Bar: max-abs error <= 1e-2 and relative L2 error <= 5e-3 of the [B, H, 512] output
+(lse within 2e-3); bitwise equality where the arithmetic is identical by construction
+(page placement, FP8 vs NVFP4 holding the same values)."""
+import numpy as np
+import pytest
+import torch
+
+import cases
+from cases import assert_parity, build_case, gpu_decode, oracle_decode, Device
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(c, splits=(0,), tag=""):
+    d = Device(c)
+    ref_out, ref_lse = oracle_decode(c)
+    res = {}
+    for s in splits:
+        out, lse = gpu_decode(c, d, num_splits=s)
+        print(f"[{tag}] splits={s} ", end="")
+        mx, rel = assert_parity(out, lse, ref_out, ref_lse, tag=f"{tag} splits={s}")
+        print(f"max-abs {mx:.2e} rel-L2 {rel:.2e}", flush=True)
+        res[s] = (out, lse)
+    return res
+
+
+def test_tiny_fp8_workload():
+    """batch 1, 16 heads, context 512, page 16 over a 1024-token pool, auto splits and one split."""
+    import synth
+    w = synth.WORKLOADS["tiny_fp8"]
+    c = build_case("fp8", [w.kv_len], w.page_size, w.seed, extra_pages=w.pool_pages - w.kv_len // w.page_size)
+    assert c.fp8_pool.shape[0] == w.pool_tokens
+    _run(c, splits=(0, 1), tag="tiny")
+
+
+@pytest.mark.parametrize("splits", [1, 2, 7, 32])
+def test_fp8_ragged_lengths_and_splits(splits):
+    c = build_case("fp8", [0, 1, 17, 64, 1000, 15, 16, 65], 16, seed=11)
+    _run(c, splits=(splits,), tag="ragged")
+
+
+@pytest.mark.parametrize("page_size", [1, 16, 64, 128])
+def test_page_sizes(page_size):
+    c = build_case("fp8", [100, 333, 64], page_size, seed=12)
+    _run(c, splits=(0, 3), tag=f"P{page_size}")
+
+
+@pytest.mark.parametrize("g", [1.0, None, 0.37])
+def test_nvfp4_parity(g):
+    c = build_case("nvfp4", [129, 700, 2048], 64, seed=13, outlier_p=0.01, g=g)
+    _run(c, splits=(0, 1, 5), tag=f"nvfp4 g={c.scale}")
+
+
+def test_bf16_parity():
+    c = build_case("bf16", [65, 500, 1], 16, seed=14)
+    _run(c, splits=(0, 1), tag="bf16")
+
+
+def test_fp8_kv_scale():
+    c = build_case("fp8", [300, 77], 16, seed=15, sigma=0.5, kv_scale=0.75)
+    _run(c, splits=(0, 2), tag="kv_scale")
+
+
+def test_32_heads():
+    c = build_case("fp8", [257, 40], 16, seed=16, heads=32)
+    _run(c, splits=(0, 1), tag="H32")
+    c = build_case("nvfp4", [190], 64, seed=17, heads=64, outlier_p=0.01)
+    _run(c, splits=(0, 3), tag="H64 nvfp4")
+
+
+def test_page_placement_is_bitwise_invariant():
+    """The same logical KV under two different physical page layouts gives identical bits."""
+    c1 = build_case("fp8", [700, 130], 16, seed=21, extra_pages=9)
+    c2 = build_case("fp8", [700, 130], 16, seed=21, extra_pages=9)
+    rng = np.random.default_rng(5)
+    perm = rng.permutation(c2.w.pool_pages).astype(np.int32)
+    new_idx = perm[c1.pt.kv_indices]
+    pool2 = np.zeros_like(c1.fp8_pool)
+    P = c1.w.page_size
+    for old, new in zip(c1.pt.kv_indices, new_idx):
+        pool2[new * P:(new + 1) * P] = c1.fp8_pool[old * P:(old + 1) * P]
+    c2.pt.kv_indices = new_idx
+    c2.fp8_pool = pool2
+    for s in (0, 1, 4):
+        o1, l1 = gpu_decode(c1, Device(c1), num_splits=s)
+        o2, l2 = gpu_decode(c2, Device(c2), num_splits=s)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2), s
+
+
+def test_fp8_and_nvfp4_bitwise_equal_on_shared_values():
+    """An FP8 pool and an NVFP4 pool (all block scales 1.0, global scale 1.0) holding the same
+    E2M1 values dequantize to the same fp16 operands, so the two decodes agree bit for bit."""
+    c = build_case("fp8", [333, 1024], 64, seed=22)
+    rng = np.random.default_rng(6)
+    codes = rng.integers(0, 16, size=c.fp8_pool.shape, dtype=np.uint8)
+    from oracle import codecs
+    vals = codecs.e2m1_decode_np(codes).astype(np.float32)
+    import synth
+    c.fp8_pool = synth.to_fp8_bytes(vals)
+    nv = build_case("nvfp4", [333, 1024], 64, seed=22)
+    nv.nv_data = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    nv.nv_scales = np.full((codes.shape[0], 36), 0x38, np.uint8)
+    nv.scale = 1.0
+    for s in (0, 1):
+        o1, l1 = gpu_decode(c, Device(c), num_splits=s)
+        o2, l2 = gpu_decode(nv, Device(nv), num_splits=s)
+        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    ref_out, ref_lse = oracle_decode(nv)
+    assert_parity(o2, l2, ref_out, ref_lse, tag="shared values")
+
+
+def test_bad_device_inputs_give_nan_not_faults():
+    """A page id outside the pool, a length above max_kv_len, a negative length and a
+    length beyond the request's pages poison only that request's outputs with NaN."""
+    c = build_case("fp8", [200, 300, 100, 50, 80], 16, seed=23, extra_pages=4)
+    ref_out, ref_lse = oracle_decode(c)
+    c.pt.kv_indices = c.pt.kv_indices.copy()
+    c.pt.kv_indices[c.pt.kv_indptr[1] + 3] = c.w.pool_pages + 5        # request 1: page out of range
+    c.pt.kv_lens = c.pt.kv_lens.copy()
+    c.pt.kv_lens[2] = -4                                                 # request 2: negative length
+    c.pt.kv_lens[3] = (c.pt.kv_indptr[4] - c.pt.kv_indptr[3]) * 16 + 1  # request 3: beyond its pages
+    for s in (0, 1):
+        out, lse = gpu_decode(c, Device(c), num_splits=s, max_kv_len=300)
+        assert np.isnan(out[1]).all() and np.isnan(lse[1]).all()
+        assert np.isnan(out[2]).all() and np.isnan(out[3]).all()
+        assert_parity(out, lse, ref_out, ref_lse, requests=[0, 4], tag="good requests")
+    c.pt.kv_lens[4] = 301                                                # above max_kv_len
+    out, lse = gpu_decode(c, Device(c), num_splits=0, max_kv_len=300)
+    assert np.isnan(out[4]).all()
+
+
+def test_nan_in_kv_propagates_to_its_request():
+    c = build_case("fp8", [100, 90], 16, seed=24)
+    rows = cases.attention.gather_rows(c.pt.kv_indptr, c.pt.kv_indices, 16, 1, 90)
+    c.fp8_pool = c.fp8_pool.copy()
+    c.fp8_pool[rows[40], 530] = 0x7F                                     # NaN in a rope dim
+    ref_out, ref_lse = oracle_decode(c)
+    assert np.isnan(ref_out[1]).all()
+    out, lse = gpu_decode(c, Device(c))
+    assert np.isnan(out[1]).all() and np.isnan(lse[1]).all()
+    assert_parity(out, lse, ref_out, ref_lse, requests=[0], tag="nan")
+
+
+def test_lse_optional_and_empty_batch():
+    import quantized_kv_paged_amd as qk
+    c = build_case("fp8", [64, 0], 16, seed=25)
+    out, lse = gpu_decode(c, Device(c), want_lse=False)
+    assert lse is None
+    assert (out[1] == 0).all()
+    ref_out, _ = oracle_decode(c)
+    assert np.abs(out - ref_out).max() <= cases.TOL_MAX_ABS
+    d = Device(c)
+    q0 = d.q[:0]
+    o, l_ = qk.mla_decode_fp8(q0, d.fp8, 1.0, d.indptr, d.indices, d.lens, 16, 64, 0.07)
+    assert o.shape == (0, 16, 512)
+
+
+def test_full_pool_cast_baseline_matches():
+    """The comparison path of the pages (whole FP8 pool -> BF16, then a 16-bit decode) gives
+    the oracle's answer too."""
+    import quantized_kv_paged_amd as qk
+    c = build_case("fp8", [500, 260], 64, seed=26, extra_pages=20)
+    d = Device(c)
+    pool_bf16 = qk.kv_dequantize(qk.MLAQ_FP8_E4M3, d.fp8, None, 1.0, qk.MLAQ_BF16)
+    out, lse = qk.mla_decode_bf16(d.q, pool_bf16, d.indptr, d.indices, d.lens, 64, c.max_kv_len, c.w.sm_scale)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = oracle_decode(c)
+    assert_parity(out.double().cpu().numpy(), lse.double().cpu().numpy(), ref_out, ref_lse, tag="cast baseline")

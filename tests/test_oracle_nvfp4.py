@@ -226,3 +226,17 @@ def test_pins_catch_planted_mistakes(monkeypatch):
             out.append((8 if math.copysign(1, v) < 0 else 0) | k)
         return sb, out
     assert not _worked_blocks_pass(ties_away)
+
+
+def test_fp32_dequant_matches_fp64_definition():
+    """At g = 1 (and any power of two) fl32(fl32(e2m1 * e4m3) * g) is exact, so it equals the
+    fp64 dequantization; the e4m3 re-encode of those values agrees with torch's cast."""
+    import torch
+    x = _random_blocks(36 * 20, 21).reshape(20, 576)
+    for g in (1.0, 0.25, 8.0):
+        data, scales = nvfp4.quantize_rows(x, g)
+        f32 = nvfp4.dequant_nvfp4_f32(data, scales, g)
+        np.testing.assert_array_equal(f32.astype(np.float64), nvfp4.dequant_nvfp4_f64(data, scales, g))
+        small = f32[np.abs(f32) <= 464]
+        ref = torch.from_numpy(small).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        np.testing.assert_array_equal(nvfp4.e4m3_encode_array(small), ref)
