@@ -174,6 +174,8 @@ def main():
     ap.add_argument("--layers", type=int, default=0, help="pool copies cycled through (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the comparison legs")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
@@ -248,6 +250,16 @@ def main():
                      "traffic": pmc_traffic(kernel_tag, kv_bytes), "kernel": "mla_decode_kernel",
                      "bytes_per_launch": kv_bytes},
     }
+
+    if args.copy_calibration:
+        # a plain copy kernel of known size: its FETCH_SIZE / WRITE_SIZE per dispatch give the
+        # counters' bytes-per-byte scale
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     if not args.no_extras and fmt == "fp8":
         # the same batch, requantized to NVFP4 with the library's own write path

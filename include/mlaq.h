@@ -77,7 +77,7 @@ typedef enum { MLAQ_BF16 = 0, MLAQ_FP8_E4M3 = 1, MLAQ_NVFP4 = 2, MLAQ_FP32 = 3 }
 typedef struct {            /* (host) */
   int32_t batch;            /* >= 0; 0 is a no-op */
   int32_t num_heads;        /* multiple of 16, 16 .. 128 */
-  int32_t page_size;        /* 1 .. 1024 tokens per page */
+  int32_t page_size;        /* tokens per page: a power of two, 1 .. 1024 */
   int32_t max_kv_len;       /* host upper bound of kv_lens[] (split planning), 0 .. MLAQ_MAX_KV_LEN */
   int64_t pool_tokens;      /* rows in the pool (> 0) */
   int32_t num_splits;       /* KV chunks per request; 0 = choose automatically */

@@ -29,7 +29,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
 
 constexpr int kTileTokens = 64;         // tokens per decode tile
-constexpr int kResidentSlots = 2 * 256; // resident decode workgroups on one MI355X (256 CUs x 2)
+constexpr int kResidentSlots = 256;     // resident decode workgroups on one MI355X (one per CU)
 
 // Split planning.  Every workgroup processes one (request, chunk, 16-head group); with all
 // requests at the host-known bound, workgroups run in "rounds" of kResidentSlots.  The cost
@@ -57,7 +57,8 @@ mlaq_status check_params(const mlaq_decode_params* p) {
   if (p->batch < 0 || p->batch > 65535) return fail(MLAQ_ERR_SHAPE, "batch %d not in [0, 65535]", p->batch);
   if (p->num_heads < 16 || p->num_heads > 128 || p->num_heads % 16)
     return fail(MLAQ_ERR_SHAPE, "num_heads %d: must be a multiple of 16 in [16, 128]", p->num_heads);
-  if (p->page_size < 1 || p->page_size > 1024) return fail(MLAQ_ERR_SHAPE, "page_size %d not in [1, 1024]", p->page_size);
+  if (p->page_size < 1 || p->page_size > 1024 || (p->page_size & (p->page_size - 1)))
+    return fail(MLAQ_ERR_SHAPE, "page_size %d: must be a power of two in [1, 1024]", p->page_size);
   if (p->max_kv_len < 0 || p->max_kv_len > MLAQ_MAX_KV_LEN)
     return fail(MLAQ_ERR_SHAPE, "max_kv_len %d not in [0, %d]", p->max_kv_len, MLAQ_MAX_KV_LEN);
   if (p->pool_tokens <= 0 || p->pool_tokens > ((int64_t)1 << 40))
@@ -124,6 +125,7 @@ mlaq_status decode_common(int fmt, const mlaq_decode_params* p, const uint16_t* 
   a.batch = p->batch;
   a.num_heads = p->num_heads;
   a.page_size = p->page_size;
+  a.page_shift = __builtin_ctz((unsigned)p->page_size);
   a.max_kv_len = p->max_kv_len;
   a.num_splits = splits;
   a.chunk_tokens = (per > 0 ? per : 1) * kTileTokens;

@@ -63,6 +63,27 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const void* p) {
       (__attribute__((address_space(3))) i16x4*)(reinterpret_cast<uintptr_t>(p)));
 }
 
+// Reductions across the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48), on the VALU:
+// with both operands equal, v_permlane16_swap returns (row pairs' even rows, odd rows) and
+// v_permlane32_swap (lower half, upper half), so op(r[0], r[1]) combines the partners
+// (lane mapping checked on gfx950 with an in-bounds index pattern).
+__device__ __forceinline__ float rows_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
+  x = fmaxf(u2f(a[0]), u2f(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+  return fmaxf(u2f(b[0]), u2f(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
+  x = u2f(a[0]) + u2f(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+  return u2f(b[0]) + u2f(b[1]);
+}
+
+// 2^x on the hardware exponential (arguments here are <= 0; results below the fp32 normal
+// range flush to zero, which only drops weights under 2^-126 of the running maximum).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // fp32 -> bf16 bits, round to nearest even, quiet NaN kept.
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   uint32_t u = f2u(x);

@@ -20,6 +20,7 @@ struct DecodeArgs {
   float* part_ml;             // [B, S, H/16, 32]: m (16) then l (16)
   int64_t pool_tokens;
   int32_t batch, num_heads, page_size, max_kv_len, num_splits, chunk_tokens;
+  int32_t page_shift;         // log2(page_size) (page sizes are powers of two)
   float score_scale;          // sm_scale * (kv scale or global scale) * log2(e)
   float out_scale;            // kv scale or global scale
 };

@@ -52,7 +52,8 @@ def _fp8(p, q=FAKE, kv=FAKE, scale=1.0, indptr=FAKE, indices=FAKE, lens=FAKE, ou
 
 @pytest.mark.parametrize("kw,status", [
     (dict(num_heads=8), ERR_SHAPE), (dict(num_heads=24), ERR_SHAPE), (dict(num_heads=144), ERR_SHAPE),
-    (dict(page_size=0), ERR_SHAPE), (dict(page_size=2048), ERR_SHAPE), (dict(batch=-1), ERR_SHAPE),
+    (dict(page_size=0), ERR_SHAPE), (dict(page_size=2048), ERR_SHAPE), (dict(page_size=48), ERR_SHAPE),
+    (dict(batch=-1), ERR_SHAPE),
     (dict(batch=70000), ERR_SHAPE), (dict(max_kv_len=-5), ERR_SHAPE), (dict(pool_tokens=0), ERR_SHAPE),
     (dict(num_splits=2000), ERR_SHAPE), (dict(sm_scale=float("nan")), ERR_VALUE),
 ])
@@ -112,7 +113,7 @@ def test_quantize_and_dequantize_validation():
 
 def test_split_planning_and_workspace():
     import synth
-    expect = {"tiny_fp8": 8, "fp8_32k": 64, "nvfp4_32k": 11, "nvfp4_160k": 51, "nvfp4_1m": 256}
+    expect = {"tiny_fp8": 8, "fp8_32k": 32, "nvfp4_32k": 29, "nvfp4_160k": 25, "nvfp4_1m": 128}
     for name, w in synth.WORKLOADS.items():
         p = _p(batch=w.batch, num_heads=w.heads, page_size=w.page_size, max_kv_len=w.kv_len,
                pool_tokens=w.pool_tokens)
