@@ -231,7 +231,7 @@ def main():
     ms, split_ms, merge_ms = timed_steps(step, n_layers, args.steps, args.warmup, hip, torch)
     achieved = kv_bytes / (split_ms * 1e-3) / 1e9
     value = kv_bytes / (ms * 1e-3) / 1e9
-    kernel_tag = f"mla_decode_kernel_{fmt}_{w.name}"
+    kernel_tag = f"mla_decode_kernel_{w.name}"
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
