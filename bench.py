@@ -54,8 +54,10 @@ class Events:
             self.ev.append(e.value)
 
     def ms(self, a, b):
+        """Elapsed ms between two recorded events; None if either was never recorded."""
         out = ctypes.c_float()
-        assert self.hip.hipEventElapsedTime(ctypes.byref(out), self.ev[a], self.ev[b]) == 0
+        if self.hip.hipEventElapsedTime(ctypes.byref(out), self.ev[a], self.ev[b]) != 0:
+            return None
         return out.value
 
     def close(self):
@@ -76,20 +78,21 @@ def timed_steps(step, n_layers, steps, warmup, hip, torch, profile=True):
     for i in range(warmup):
         step(i % n_layers)
     torch.cuda.synchronize()
-    ev = Events(hip, 3 * steps) if profile else None
+    ev = Events(hip, 4 * steps) if profile else None
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for i in range(steps):
         if profile:
-            qk.mlaq_set_profile_events(ev.ev[3 * i], ev.ev[3 * i + 1], ev.ev[3 * i + 2])
+            qk.mlaq_set_profile_events(*ev.ev[4 * i:4 * i + 4])
         step(i % n_layers)
     end.record()
     torch.cuda.synchronize()
     total = start.elapsed_time(end) / steps
     split = merge = None
     if profile:
-        split = float(np.mean([ev.ms(3 * i, 3 * i + 1) for i in range(steps)]))
-        merge = float(np.mean([ev.ms(3 * i + 1, 3 * i + 2) for i in range(steps)]))
+        split = float(np.mean([ev.ms(4 * i, 4 * i + 1) for i in range(steps)]))
+        merges = [m for m in (ev.ms(4 * i + 2, 4 * i + 3) for i in range(steps)) if m is not None]
+        merge = float(np.mean(merges)) if merges else 0.0
         ev.close()
     return total, split, merge
 

@@ -137,12 +137,14 @@ mlaq_status kv_dequantize(mlaq_format src_format, const uint8_t* kv_data, const 
                           const int64_t* rows, int64_t num_rows, int64_t pool_tokens, mlaq_format dst_format,
                           void* dst, hipStream_t stream);
 
-/* (host) Profiling hook for callers that time the kernels themselves.  Registers up to three
- * HIP events (hipEvent_t, or NULL) for the NEXT decode call made on this thread: it records
- * `before_split` on its stream before the split-KV kernel, `after_split` after it (before
- * the merge kernel, if any) and `after_merge` after the last kernel; then the registration
- * is cleared.  The events are owned by the caller. */
-mlaq_status mlaq_set_profile_events(hipEvent_t before_split, hipEvent_t after_split, hipEvent_t after_merge);
+/* (host) Profiling hook for callers that time the kernels themselves.  Registers up to four
+ * HIP events (hipEvent_t, or NULL) for the NEXT decode call made on this thread: the split-KV
+ * kernel is launched with `split_start` / `split_end` recorded at its own start and end
+ * (hipExtLaunchKernelGGL), and the merge kernel, if the call runs one, with `merge_start` /
+ * `merge_end`; then the registration is cleared.  A call without a merge kernel leaves the
+ * merge events untouched.  The events are owned by the caller. */
+mlaq_status mlaq_set_profile_events(hipEvent_t split_start, hipEvent_t split_end, hipEvent_t merge_start,
+                                    hipEvent_t merge_end);
 
 /* (host) Message for the last non-OK status returned on this thread ("" if none). */
 const char* mlaq_last_error(void);

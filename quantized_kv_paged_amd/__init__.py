@@ -43,7 +43,7 @@ _SIGS = {
     "mla_decode_bf16": ([_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "kv_quantize_nvfp4": ([_vp, ctypes.c_int, _f32, _i64, _vp, _vp, _vp, _i64, _f32, _vp], ctypes.c_int),
     "kv_dequantize": ([ctypes.c_int, _vp, _vp, _f32, _vp, _i64, _i64, ctypes.c_int, _vp, _vp], ctypes.c_int),
-    "mlaq_set_profile_events": ([_vp, _vp, _vp], ctypes.c_int),
+    "mlaq_set_profile_events": ([_vp, _vp, _vp, _vp], ctypes.c_int),
     "mlaq_last_error": ([], ctypes.c_char_p),
     "mlaq_version": ([], ctypes.c_char_p),
 }
@@ -75,9 +75,10 @@ def _stream(stream):
     return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
 
 
-def mlaq_set_profile_events(before_split, after_split, after_merge) -> None:
-    """Raw hipEvent_t handles (ints or None) recorded by the next decode call on this thread."""
-    _check(_lib.mlaq_set_profile_events(before_split, after_split, after_merge))
+def mlaq_set_profile_events(split_start, split_end, merge_start=None, merge_end=None) -> None:
+    """Raw hipEvent_t handles (ints or None) recorded at the start and end of the kernels of the
+    next decode call on this thread."""
+    _check(_lib.mlaq_set_profile_events(split_start, split_end, merge_start, merge_end))
 
 
 def version() -> str:

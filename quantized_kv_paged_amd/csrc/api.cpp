@@ -147,10 +147,12 @@ const char* mlaq_last_error(void) { return g_err.c_str(); }
 
 const char* mlaq_version(void) { return "mlaq 0.1 gfx950"; }
 
-mlaq_status mlaq_set_profile_events(hipEvent_t before_split, hipEvent_t after_split, hipEvent_t after_merge) {
-  g_events.before_split = before_split;
-  g_events.after_split = after_split;
-  g_events.after_merge = after_merge;
+mlaq_status mlaq_set_profile_events(hipEvent_t split_start, hipEvent_t split_end, hipEvent_t merge_start,
+                                    hipEvent_t merge_end) {
+  g_events.split_start = split_start;
+  g_events.split_end = split_end;
+  g_events.merge_start = merge_start;
+  g_events.merge_end = merge_end;
   return MLAQ_OK;
 }
 

@@ -26,7 +26,7 @@ struct DecodeArgs {
 };
 
 struct ProfileEvents {
-  hipEvent_t before_split = nullptr, after_split = nullptr, after_merge = nullptr;
+  hipEvent_t split_start = nullptr, split_end = nullptr, merge_start = nullptr, merge_end = nullptr;
 };
 hipError_t launch_decode(int fmt, const DecodeArgs& a, hipStream_t stream, const ProfileEvents& ev);
 
