@@ -28,8 +28,8 @@ mlaq_status fail(mlaq_status s, const char* fmt, ...) {
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
 
-constexpr int kTileTokens = 64;         // tokens per decode tile
-constexpr int kResidentSlots = 256;     // resident decode workgroups on one MI355X (one per CU)
+constexpr int kTileTokens = mlaq::kDecodeTile;   // tokens per decode tile
+constexpr int kResidentSlots = mlaq::kComputeUnits * mlaq::kDecodeGroupsPerCu;   // resident decode workgroups
 
 // Split planning.  Every workgroup processes one (request, chunk, 16-head group); with all
 // requests at the host-known bound, workgroups run in "rounds" of kResidentSlots.  The cost

@@ -9,26 +9,33 @@
 // (aitop.news, implementation item 3) describes for decode: packed tiles and E4M3 block
 // scales read as stored, converted in registers, global scale applied as a scalar factor.
 //
-// gfx950 design: one workgroup of 8 waves = one request x one KV chunk x 16 heads, one
-// workgroup per CU.
+// gfx950 design: one workgroup of 4 waves = one request x one KV chunk x 16 heads; two
+// workgroups share a CU (80 KB of LDS and at most 256 VGPRs each), so every SIMD runs two
+// waves of independent workgroups.
 //   * every head shares the single latent KV row, so each KV byte is read from HBM once and
 //     both products are dense 16-head contractions on MFMA;
-//   * tile = 64 tokens.  Wave w = (token group tg = w % 4, dim half dh = w / 4).  S^T = K Q^T
+//   * tile = 64 tokens.  Wave w = (token group tg = w % 2, dim half dh = w / 2) owns tokens
+//     32tg .. 32tg+31 of each tile as two 16-token MFMA blocks.  S^T = K Q^T
 //     (v_mfma_f32_16x16x32) is split over the pair (tg, 0) / (tg, 1): half dh is value dims
 //     256dh .. 256dh+255 plus rope dims 512+32dh .. +31; each wave holds that half of the query
-//     operand and converts that half of each of its group's 16 rows, and the pair swaps 1 KB
-//     of partial scores through LDS;
-//   * each token group is its own online-softmax stream over the chunk; its probabilities are
-//     already in the layout of the A operand of v_mfma_f32_16x16x16 (lane = head, 4 tokens),
-//     so O += P V needs no score traffic: wave (tg, dh) accumulates the 256 value dims of half
-//     dh over its 16 tokens, the V operand coming from LDS with one gfx950 transposed read
-//     (ds_read_b64_tr_b16) per 16 dims.  The four streams are merged in LDS at the end;
-//   * K rows go global -> VGPR with 8/16-byte loads issued one tile ahead (two register
-//     buffers), and are converted to fp16 in registers (FP8: exact; NVFP4: E2M1 -> fp16 times
-//     the fp16 E4M3 block scale, exact since every E2M1 x E4M3 product is an fp16 value); the
-//     converted operand feeds the QK MFMA directly and its value dims are written once to an
-//     XOR-swizzled LDS tile;
-//   * LDS tiles are double-buffered, so one barrier per tile suffices;
+//     operand and converts that half of its 32 rows, and the pair swaps 2 KB of partial scores
+//     through LDS (double-buffered, one barrier per tile);
+//   * each token group is its own online-softmax stream over the chunk; its 32 probabilities
+//     per head are already in the A-operand layout of a 32-token v_mfma_f32_16x16x32 (lane =
+//     head, 8 tokens), so O += P V needs no score traffic: wave (tg, dh) accumulates the 256
+//     value dims of half dh over its 32 tokens, the V operand coming from LDS with two gfx950
+//     transposed reads (ds_read_b64_tr_b16) per 16 dims.  The two streams are merged in LDS at
+//     the end of the chunk;
+//   * K rows go global -> VGPR: for pages of at least 64 tokens a tile is 64 contiguous pool
+//     rows, read with buffer loads through a per-tile descriptor whose size admits only the
+//     tile's valid rows (other lanes read zeros); the registers of a tile are refilled with
+//     the next tile's loads as soon as they are converted, so the loads are in flight during
+//     the softmax and PV of the tile.  Rows are converted to fp16 in registers (FP8: exact;
+//     NVFP4: E2M1 -> fp16 times the fp16 E4M3 block scale, exact since every E2M1 x E4M3
+//     product is an fp16 value); the converted operand feeds the QK MFMA directly and its value
+//     dims are written once to an XOR-swizzled LDS tile;
+//   * a wave reads back only the value dims it wrote itself, so each wave has a private
+//     single-buffered LDS value tile (LDS operations of one wave complete in order);
 //   * the per-tensor FP8 scale or NVFP4 global scale and a power-of-two query prescale
 //     (bf16 queries are converted to fp16 exactly) fold into the score and output scales.
 #include <hip/hip_ext.h>
@@ -39,10 +46,21 @@
 
 namespace mlaq {
 
-constexpr int kTile = 64;       // tokens per tile
-constexpr int kWaves = 8;
+constexpr int kStreams = 2;                // online-softmax streams (token groups) per workgroup
+constexpr int kBlocks = 2;                 // 16-token MFMA blocks per wave per tile
+constexpr int kTile = 16 * kBlocks * kStreams;   // tokens per tile
+constexpr int kWaves = 2 * kStreams;       // (token group, dim half) pairs
 constexpr int kThreads = 64 * kWaves;
-constexpr int kVRow = 1024;     // bytes per LDS value row (512 16-bit dims); 16-B chunks XOR-swizzled
+static_assert(kTile == kDecodeTile, "tile size shared with the host planner");
+constexpr int kVRow = 512;                 // bytes per LDS value row of a wave (its 256 fp16 dims)
+constexpr int kWaveV = 16 * kBlocks * kVRow;       // a wave's value tile (16 KB)
+constexpr int kSwapW = kBlocks * 64 * 16;          // bytes of a wave's partial scores (2 KB)
+constexpr int kSwap = kWaves * kWaveV;             // byte offset of the swap buffers [2][kWaves]
+constexpr int kSmem = kSwap + 2 * kWaves * kSwapW; // 80 KB: two workgroups share a CU
+constexpr int kORow = 260;                 // fp32 row stride of the end-of-chunk merge buffer (padded)
+constexpr int kMLOff = kSmem - kStreams * 2 * 16 * 4;   // byte offset of the streams' (m, l)
+static_assert(kStreams * 16 * kORow * 4 <= kMLOff, "merge buffer overlaps the (m, l) table");
+static_assert(2 * kSmem <= 160 * 1024, "two workgroups per CU");
 constexpr float kMinusBig = -3.0e38f;   // initial running max: finite, so an empty stream stays finite
 constexpr float kSlack = 8.0f;          // lazy-rescale threshold of the running max (log2 units)
 
@@ -58,13 +76,13 @@ template <> struct RawTile<FMT_BF16> { u32x4 d[9]; };                           
 template <int FMT> struct OpType { typedef f16x8 type; typedef _Float16 elem; };
 template <> struct OpType<FMT_BF16> { typedef bf16x8 type; typedef __bf16 elem; };
 
-// LDS value tile: row r (token) of 1024 B holds dims 0..511; its 16-byte chunk c is stored at
-// chunk c ^ vswz(r), vswz(r) = x ^ 2x (mod 16) for x = r mod 16.  The 16-byte row writes of the
-// QK phase (16 rows x 4 chunks per instruction) and the transposed 8-byte reads of the PV phase
-// (16 rows x 2 chunks) then spread over all banks for any grouping of the wave's lanes into
-// 256-byte (64 banks) or 128-byte (32 banks) cycles (checked by enumeration).  Since the XOR
-// only touches chunk bits 0-3, every address is one per-lane base XOR a per-instruction
-// constant in bits 4-7, plus a constant offset.
+// A wave's LDS value tile: row r (its token 16tg + r) of 512 B holds its 256 value dims; the
+// 16-byte chunk c is stored at chunk c ^ vswz(r), vswz(r) = x ^ 2x (mod 16) for x = r mod 16.
+// The 16-byte row writes of the QK phase (16 rows x 4 chunks per instruction) and the
+// transposed 8-byte reads of the PV phase (16 rows x 2 chunks) then spread over all banks for
+// any grouping of the wave's lanes into 256-byte (64 banks) or 128-byte (32 banks) cycles
+// (checked by enumeration).  Since the XOR only touches chunk bits 0-3, every address is one
+// per-lane base XOR a per-instruction constant in bits 4-7, plus a constant offset.
 __device__ __forceinline__ int vswz(int r) { const int x = r & 15; return (x ^ (x << 1)) & 15; }
 
 __device__ __forceinline__ int kb_dim(int dh, int kb, int g) {
@@ -140,6 +158,57 @@ __device__ __forceinline__ void load_raw(RawTile<FMT>& r, const DecodeArgs& a, i
   }
 }
 
+// Same loads for a tile whose rows are contiguous in the pool: buffer loads through
+// descriptors whose base is the tile's first row (kv, and the NVFP4 scales in sc) and whose
+// size covers only the tile's valid rows, so the lanes of other rows read zeros; the lane's
+// constant byte offsets are o.v (value part), o.e (rope part), o.s (NVFP4 scales, row share).
+struct LaneOffsets { uint32_t v, e, s; };
+template <int FMT>
+__device__ __forceinline__ LaneOffsets lane_offsets(int tok_in_tile, int dh, int g) {
+  LaneOffsets o;
+  if constexpr (FMT == FMT_FP8) {
+    o.v = tok_in_tile * kD + 256 * dh + 16 * g;
+    o.e = tok_in_tile * kD + 512 + 32 * dh + 8 * g;
+    o.s = 0;
+  } else if constexpr (FMT == FMT_NVFP4) {
+    o.v = tok_in_tile * kNvData + 128 * dh + 8 * g;
+    o.e = tok_in_tile * kNvData + 256 + 16 * dh + 4 * g;
+    o.s = tok_in_tile * kNvScale + 16 * dh;
+  } else {
+    o.v = 2 * (tok_in_tile * kD + 256 * dh + 16 * g);
+    o.e = 2 * (tok_in_tile * kD + 512 + 32 * dh + 8 * g);
+    o.s = 0;
+  }
+  return o;
+}
+
+template <int FMT>
+__device__ __forceinline__ void load_raw_tile(RawTile<FMT>& r, BufferRsrc kv, BufferRsrc sc, const LaneOffsets& o,
+                                              int dh, int tok0) {
+  if constexpr (FMT == FMT_FP8) {
+    const uint32_t so = tok0 * kD;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) r.d[m] = buffer_load_b128(kv, o.v + 64 * m, so);
+    r.e = buffer_load_b64(kv, o.e, so);
+  } else if constexpr (FMT == FMT_NVFP4) {
+    const uint32_t so = tok0 * kNvData, ss = tok0 * kNvScale;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) r.d[m] = buffer_load_b64(kv, o.v + 32 * m, so);
+    r.e = buffer_load_b32(kv, o.e, so);
+    const u32x4 s4 = buffer_load_b128(sc, o.s, ss);          // blocks 16dh .. 16dh+15
+    r.s[0] = s4[0]; r.s[1] = s4[1]; r.s[2] = s4[2]; r.s[3] = s4[3];
+    r.s[4] = buffer_load_b32(sc, o.s - 16 * dh + 32, ss);    // rope blocks 32 .. 35
+  } else {
+    const uint32_t so = tok0 * 2 * kD;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      r.d[2 * m] = buffer_load_b128(kv, o.v + 128 * m, so);
+      r.d[2 * m + 1] = buffer_load_b128(kv, o.v + 128 * m + 16, so);
+    }
+    r.d[8] = buffer_load_b128(kv, o.e, so);
+  }
+}
+
 // Replace the data of masked lanes by zeros and of bad-page lanes by NaN codes.
 template <int FMT>
 __device__ __forceinline__ void fix_raw(RawTile<FMT>& r, int state) {
@@ -191,14 +260,6 @@ __device__ __forceinline__ typename OpType<FMT>::type dequant(const RawTile<FMT>
   }
 }
 
-typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ f32x4 mfma16x16x16(f16x4_t a, i16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma16x16x16(i16x4 a, i16x4 b, f32x4 c) {   // bf16 bits
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
@@ -208,17 +269,15 @@ __device__ __forceinline__ float wave_max(float v) {
 template <int FMT, bool DIRECT, bool TILEPAGE>
 __global__ __launch_bounds__(kThreads, 2) void mla_decode_kernel(DecodeArgs a) {
   typedef typename OpType<FMT>::type Op;
-  typedef typename OpType<FMT>::elem Elem;
-  typedef typename std::conditional<FMT == FMT_BF16, i16x4, f16x4_t>::type Pop;
-  // value tiles (2 x 64 KB), reused as the 4-stream output buffer at the end; partial scores
-  // of every wave (2 x 8 x 1 KB); per-stream running max / sum
-  __shared__ __attribute__((aligned(16))) char sV[2][kTile * kVRow];
-  __shared__ __attribute__((aligned(16))) float sX[2][kWaves][256];
-  __shared__ float sML[4][2][16];
+  // raw tiles in flight per wave: two for the 8-bit and 4-bit pools, one for the 16-bit pool
+  constexpr int kBufs = 1;
+  // the waves' value tiles (4 x 16 KB) and the partial-score swap buffers (2 x 4 x 2 KB); at
+  // the end of the chunk, the streams' output buffer of one dim half and their (m, l)
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
 
   const int split = blockIdx.x, b = blockIdx.y, hg = blockIdx.z;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
-  const int tg = w & 3, dh = w >> 2;
+  const int tg = w % kStreams, dh = w / kStreams;   // the pair partner is w ^ kStreams
   const int H = a.num_heads;
 
   // ---- request bounds (device data, checked without faulting)
@@ -254,17 +313,48 @@ __global__ __launch_bounds__(kThreads, 2) void mla_decode_kernel(DecodeArgs a) {
 #pragma unroll
   for (int nt = 0; nt < 16; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int my_tok = 16 * tg + l16;
-  RawTile<FMT> bufA, bufB;
-  int stA, stB = 0;
+  // the lane's token of block tb of a tile: 32tg + 16tb + l16
+  const int my_tok = 16 * kBlocks * tg + l16;
+  char* const vt = smem + w * kWaveV;
+  float* const sX = reinterpret_cast<float*>(smem + kSwap);
+  RawTile<FMT> rawA[kBlocks], rawB[kBlocks];
+  int stA[kBlocks], stB[kBlocks];
   // prologue, ordered for the in-order load counter: the first two page-table batches, this
-  // wave's half of the query rows, then tile 0's rows; the query is converted while those are
-  // in flight
+  // wave's half of the query rows, then the first tiles' rows; the query is converted while
+  // those are in flight
   PageWindow pw;
   pw.init(a, p0, npages, t_begin, lane);
-  auto row_of = [&](int t0, int& st) __attribute__((always_inline)) {   // row of the lane's token of tile t0
-    const int page = pw.page<TILEPAGE>(a, TILEPAGE ? t0 : t0 + my_tok, lane);
-    return tile_row(a, npages, t0 + my_tok, t_end, page, st);
+  const LaneOffsets lofs = lane_offsets<FMT>(my_tok, dh, grp);
+  constexpr int kRowBytes = FMT == FMT_FP8 ? kD : FMT == FMT_NVFP4 ? kNvData : 2 * kD;
+  // loads of the lane's share of tile t0 (both blocks) into r, validity states into s
+  // (0 valid, 1 past the chunk, 2 no valid row; see tile_row)
+  auto fetch = [&](RawTile<FMT>(&r)[kBlocks], int(&s)[kBlocks], int t0) __attribute__((always_inline)) {
+    if constexpr (TILEPAGE) {
+      // all lanes share the page: the tile's valid rows (tokens before t_end, rows inside the
+      // pool) are rows row0 .. row0 + nvalid - 1; lanes of other rows read zeros through the
+      // descriptors' size limit, which fix_raw keeps (past the chunk) or replaces by NaN codes
+      const int page = pw.page<true>(a, t0, lane);
+      const int64_t row0 = ((int64_t)page << a.page_shift) + (t0 & (a.page_size - 1));
+      const int64_t room = page >= 0 ? a.pool_tokens - row0 : 0;
+      const int nvalid = (int)max((int64_t)0, min((int64_t)min(kTile, t_end - t0), room));
+      const int64_t rbase = nvalid > 0 ? row0 : 0;
+      const BufferRsrc kv = make_rsrc(a.kv + rbase * kRowBytes, nvalid * kRowBytes);
+      const BufferRsrc sc = make_rsrc(FMT == FMT_NVFP4 ? a.kv_scales + rbase * kNvScale : a.kv,
+                                      FMT == FMT_NVFP4 ? nvalid * kNvScale : 0);
+#pragma unroll
+      for (int tb = 0; tb < kBlocks; ++tb) {
+        const int tt = my_tok + 16 * tb;
+        s[tb] = t0 + tt >= t_end ? 1 : (tt >= nvalid ? 2 : 0);
+        load_raw_tile<FMT>(r[tb], kv, sc, lofs, dh, 16 * tb);
+      }
+    } else {
+#pragma unroll
+      for (int tb = 0; tb < kBlocks; ++tb) {
+        const int tok = t0 + my_tok + 16 * tb;
+        const int page = pw.page<false>(a, tok, lane);
+        load_raw<FMT>(r[tb], a, tile_row(a, npages, tok, t_end, page, s[tb]), dh, grp);
+      }
+    }
   };
   u32x4 qraw[9];
   {
@@ -272,7 +362,10 @@ __global__ __launch_bounds__(kThreads, 2) void mla_decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int kb = 0; kb < 9; ++kb) qraw[kb] = *reinterpret_cast<const u32x4*>(qrow + kb_dim(dh, kb, grp));
   }
-  load_raw<FMT>(bufA, a, row_of(t_begin, stA), dh, grp);
+  fetch(rawA, stA, t_begin);
+  if constexpr (kBufs == 2) {
+    if (ntiles > 1) fetch(rawB, stB, t_begin + kTile);
+  }
 
   Op qop[9];
   float score_scale = a.score_scale;
@@ -316,58 +409,90 @@ __global__ __launch_bounds__(kThreads, 2) void mla_decode_kernel(DecodeArgs a) {
     ssel[0] = b0 | (b0 << 8) | 0x0c0c0000u;
     ssel[1] = b1 | (b1 << 8) | 0x0c0c0000u;
   }
-  // LDS byte addresses.  Value writes of k-block 2m + h: row my_tok, chunk
-  // 32dh + 16(m >> 1) + ((8(m & 1) | 2g | h) ^ vswz(my_tok)), i.e. vwb ^ 16(8(m & 1) | h), plus
-  // 256(m >> 1).  Transposed reads of dims 256dh + 16nt + 4q .. +3 by lane (g, 4i + q): row
-  // 16tg + 4g + i, chunk 32dh + 16(nt >> 3) + ((2(nt & 7) | (q >> 1)) ^ vswz(row)), i.e.
-  // vrb ^ 32(nt & 7), plus 256(nt >> 3).
-  const int vwb = my_tok * kVRow + 512 * dh + 16 * ((2 * grp) ^ vswz(my_tok));
-  const int q4 = l16 & 3, vrow = 16 * tg + 4 * grp + (l16 >> 2);
-  const int vrb = vrow * kVRow + 512 * dh + 16 * ((q4 >> 1) ^ vswz(vrow)) + 8 * (q4 & 1);
+  // Byte addresses in the wave's value tile (rows = its 32 tokens 16tb + r, dims relative to
+  // 256dh).  Writes of k-block 2m + h of block tb: row 16tb + l16, chunk
+  // 16(m >> 1) + ((8(m & 1) | 2g | h) ^ vswz(l16)), i.e. vwb ^ 16(8(m & 1) | h), plus
+  // 256(m >> 1) + 16 kVRow tb.  Transposed reads of dims 16nt + 4q .. +3 of block tb by lane
+  // (g, 4i + q): row 16tb + 4g + i, chunk 16(nt >> 3) + ((2(nt & 7) | (q >> 1)) ^ vswz(row)),
+  // i.e. vrb ^ 32(nt & 7), plus 256(nt >> 3) + 16 kVRow tb.
+  const int vwb = l16 * kVRow + 16 * ((2 * grp) ^ vswz(l16));
+  const int q4 = l16 & 3, vrow = 4 * grp + (l16 >> 2);
+  const int vrb = vrow * kVRow + 16 * ((q4 >> 1) ^ vswz(vrow)) + 8 * (q4 & 1);
 
-  auto compute = [&](RawTile<FMT>& cur, int st, int t0, int buf) __attribute__((always_inline)) {
-    if (__any(st != 0)) fix_raw<FMT>(cur, st);
-    char* v = sV[buf];
-    // partial S^T over this wave's dim half for its 16 tokens; value dims to LDS
-    f32x4 sacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};   // two MFMA chains
-#define MLAQ_QK_STEP(KB)                                                          \
-    {                                                                             \
-      const Op kop = dequant<FMT, KB>(cur, ssel);                                 \
-      sacc[KB & 1] = mfma16x16x32(kop, qop[KB], sacc[KB & 1]);                    \
-      if (KB < 8)                                                                 \
-        *reinterpret_cast<Op*>(v + ((vwb ^ (16 * ((KB & 2) * 4 + (KB & 1)))) + 256 * (KB >> 2))) = kop; \
+  // One tile: partial S^T of this wave's dim half for its two token blocks (value dims to
+  // LDS), refill of the raw buffer with the tile kBufs ahead, swap of partial scores with the
+  // pair partner, online softmax of the stream, O += P V over the wave's dim half.
+  auto compute = [&](RawTile<FMT>(&cur)[kBlocks], int(&st)[kBlocks], int t0, int buf, bool more)
+                     __attribute__((always_inline)) {
+#pragma unroll
+    for (int tb = 0; tb < kBlocks; ++tb)
+      if (__any(st[tb] != 0)) fix_raw<FMT>(cur[tb], st[tb]);
+    f32x4 sacc[kBlocks];
+#pragma unroll
+    for (int tb = 0; tb < kBlocks; ++tb) sacc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#define MLAQ_QK_STEP(KB)                                                                          \
+    _Pragma("unroll") for (int tb = 0; tb < kBlocks; ++tb) {                                      \
+      const Op kop = dequant<FMT, KB>(cur[tb], ssel);                                             \
+      sacc[tb] = mfma16x16x32(kop, qop[KB], sacc[tb]);                                            \
+      if (KB < 8)                                                                                 \
+        *reinterpret_cast<Op*>(vt + ((vwb ^ (16 * ((KB & 2) * 4 + (KB & 1)))) + 256 * (KB >> 2) + \
+                                     16 * kVRow * tb)) = kop;                                     \
     }
     MLAQ_QK_STEP(0) MLAQ_QK_STEP(1) MLAQ_QK_STEP(2) MLAQ_QK_STEP(3) MLAQ_QK_STEP(4)
     MLAQ_QK_STEP(5) MLAQ_QK_STEP(6) MLAQ_QK_STEP(7) MLAQ_QK_STEP(8)
 #undef MLAQ_QK_STEP
-    // lane: head l16, tokens 16tg + 4grp + i
-    f32x4 sp;
-    {
-      const f32x4 s = sacc[0] + sacc[1];
+    // the raw tile is converted: its registers take the loads of the tile kBufs ahead, which
+    // are in flight during this tile's softmax and PV and the next tiles
+    if (more) fetch(cur, st, t0 + kBufs * kTile);
+    // lane: head l16, tokens 32tg + 16tb + 4grp + i
+    f32x4 sp[kBlocks];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = t0 + 16 * tg + 4 * grp + i;
-        sp[i] = tok < t_end ? s[i] * score_scale : -INFINITY;
-      }
-      *reinterpret_cast<f32x4*>(&sX[buf][w][4 * lane]) = sp;
+    for (int tb = 0; tb < kBlocks; ++tb) sp[tb] = sacc[tb] * score_scale;
+    if (t0 + kTile > t_end) {   // partial tile (uniform)
+#pragma unroll
+      for (int tb = 0; tb < kBlocks; ++tb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (t0 + my_tok - l16 + 16 * tb + 4 * grp + i >= t_end) sp[tb][i] = -INFINITY;
     }
-    __syncthreads();
-    const f32x4 sq = *reinterpret_cast<const f32x4*>(&sX[buf][w ^ 4][4 * lane]);
-    // value operands of the first 8 dim blocks (issued before the softmax arithmetic so their
-    // latency overlaps it)
-    i16x4 vop[8];
+    // swap partial scores with the other half of the pair (buffer buf alternates with the
+    // tiles: a wave reaches this barrier again only after its partner has read the previous
+    // contents of the other buffer)
+    float* const xw = sX + (buf * kWaves + w) * (kSwapW / 4);
+    float* const xp = sX + (buf * kWaves + (w ^ kStreams)) * (kSwapW / 4);
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) vop[nt] = lds_read_tr16(v + (vrb ^ (32 * nt)));
+    for (int tb = 0; tb < kBlocks; ++tb) *reinterpret_cast<f32x4*>(xw + 256 * tb + 4 * lane) = sp[tb];
+    __syncthreads();
+    f32x4 sq[kBlocks];
+#pragma unroll
+    for (int tb = 0; tb < kBlocks; ++tb) sq[tb] = *reinterpret_cast<const f32x4*>(xp + 256 * tb + 4 * lane);
+    // value operands of the first dim blocks, issued before the softmax arithmetic so that
+    // their latency overlaps it.  Dim block nt of token block tb is at vrb ^ 32(nt & 7), plus
+    // 256(nt >> 3) + 16 kVRow tb; the operand of the 32-token product is the pair of reads.
+    constexpr int kVAhead = 3;
+    auto vread = [&](int nt) __attribute__((always_inline)) {
+      const char* p = vt + (vrb ^ (32 * (nt & 7))) + 256 * (nt >> 3);
+      const i16x4 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 16 * kVRow);
+      return i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    };
+    i16x8 vop[16];
+#pragma unroll
+    for (int nt = 0; nt < kVAhead; ++nt) vop[nt] = vread(nt);
 
     // online softmax of this stream (both waves of the pair compute the same values:
     // sp + sq and sq + sp round identically)
-    float sc[4];
+    float sc[4 * kBlocks];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sc[i] = sp[i] + sq[i];
+    for (int tb = 0; tb < kBlocks; ++tb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[4 * tb + i] = sp[tb][i] + sq[tb][i];
     // The reference point m_run of the exponentials moves only when a score exceeds it by more
     // than kSlack (log2 units), so probabilities stay below 2^kSlack (exact in fp16 / bf16 and
     // far from overflow in the fp32 sums) and the accumulators are rescaled only then.
-    const float tmax = rows_max(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
+    float lmax = sc[0];
+#pragma unroll
+    for (int j = 1; j < 4 * kBlocks; ++j) lmax = fmaxf(lmax, sc[j]);
+    const float tmax = rows_max(lmax);
     const bool grow = tmax > m_run + kSlack;
     if (__any(grow)) {
       const float m_new = grow ? tmax : m_run;
@@ -381,96 +506,110 @@ __global__ __launch_bounds__(kThreads, 2) void mla_decode_kernel(DecodeArgs a) {
         for (int nt = 0; nt < 16; ++nt) o[nt][i] *= ai;
       }
     }
-    Pop pop;
+    // P in the A-operand layout of the 32-token product: lane (g, head l16) holds k-indices
+    // 8g .. 8g+7 = tokens 4g .. 4g+3 of block 0, then 4g .. 4g+3 of block 1
+    Op pop;
     float rsum = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float pe = fast_exp2(sc[i] - m_run);
+    for (int j = 0; j < 4 * kBlocks; ++j) {
+      const float pe = fast_exp2(sc[j] - m_run);
       rsum += pe;
-      if constexpr (FMT == FMT_BF16) pop[i] = (short)f32_to_bf16_rne(pe);
-      else pop[i] = (_Float16)pe;
+      if constexpr (FMT == FMT_BF16) pop[j] = (__bf16)pe;
+      else pop[j] = (_Float16)pe;
     }
     l_run += rows_sum(rsum);
-    // O += P V: 16 dims per MFMA, K = this group's 16 tokens; the operands of dim blocks 8-15
-    // are read while the first 8 products run
-    i16x4 vop2[8];
+    // O += P V: 16 dims per product, K = this group's 32 tokens; each operand is read kVAhead
+    // products ahead of its use
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt) vop2[nt] = lds_read_tr16(v + (vrb ^ (32 * nt)) + 256);
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) o[nt] = mfma16x16x16(pop, vop[nt], o[nt]);
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt) o[8 + nt] = mfma16x16x16(pop, vop2[nt], o[8 + nt]);
+    for (int nt = 0; nt < 16; ++nt) {
+      if (nt + kVAhead < 16) vop[nt + kVAhead] = vread(nt + kVAhead);
+      o[nt] = mfma16x16x32(pop, __builtin_bit_cast(Op, vop[nt]), o[nt]);
+    }
   };
 
-  // ---- tile pipeline: two register buffers alternate (A holds even tiles, B odd ones);
-  //      while one tile is computed, the other's loads are in flight.
-  //      Loads are issued unconditionally (lanes without a valid row read row 0), so the code
-  //      between issue and use is straight-line.  LDS tiles alternate with the tiles.
-  if constexpr (FMT == FMT_BF16) {
-    // 16-bit pool (comparison path): one register buffer
-    for (int k = 0; k < ntiles; ++k) {
-      const int t0 = t_begin + k * kTile;
-      compute(bufA, stA, t0, k & 1);
-      if (k + 1 >= ntiles) break;
-      load_raw<FMT>(bufA, a, row_of(t0 + kTile, stA), dh, grp);
-    }
+  // ---- tile loop: kBufs raw buffers per wave, each refilled (with the tile kBufs ahead) as
+  //      soon as its tile is converted.  The score swap buffers alternate with the tiles.
+  if constexpr (kBufs == 1) {
+    for (int k = 0; k < ntiles; ++k) compute(rawA, stA, t_begin + k * kTile, k & 1, k + 1 < ntiles);
   } else {
     for (int k = 0; k < ntiles; k += 2) {
       const int t0 = t_begin + k * kTile;
-      load_raw<FMT>(bufB, a, row_of(t0 + kTile, stB), dh, grp);
-      compute(bufA, stA, t0, 0);
+      compute(rawA, stA, t0, 0, k + 2 < ntiles);
       if (k + 1 >= ntiles) break;
-      load_raw<FMT>(bufA, a, row_of(t0 + 2 * kTile, stA), dh, grp);
-      compute(bufB, stB, t0 + kTile, 1);
+      compute(rawB, stB, t0 + kTile, 1, k + 3 < ntiles);
     }
   }
 
-  // ---- merge the four token-group streams in LDS.  Stream tg: running max m_tg, sum l_tg;
-  //      weights w_tg = 2^(m_tg - M), M = max_tg m_tg; L = sum_tg w_tg l_tg.
-  __syncthreads();                                   // all value-tile reads are done
-  if (dh == 0 && grp == 0) { sML[tg][0][l16] = m_run; sML[tg][1][l16] = l_run; }
+  // ---- merge the token-group streams in LDS.  Stream tg: running max m_tg, sum l_tg;
+  //      weights w_tg = 2^(m_tg - M), M = max_tg m_tg; L = sum_tg w_tg l_tg.  The weighted
+  //      outputs of one dim half at a time go through a [tg][head][256] buffer (rows padded to
+  //      kORow floats so the four lane groups of a write hit different banks).
+  __syncthreads();                                   // all value-tile and swap reads are done
+  float* const sML = reinterpret_cast<float*>(smem + kMLOff);   // [tg][m, l][head]
+  if (dh == 0 && grp == 0) { sML[tg * 32 + l16] = m_run; sML[tg * 32 + 16 + l16] = l_run; }
   __syncthreads();
-  float* sO = reinterpret_cast<float*>(&sV[0][0]);   // [tg][head][512] fp32 = 128 KB
-  {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 4 * grp + i;
-      const float M = fmaxf(fmaxf(sML[0][0][h], sML[1][0][h]), fmaxf(sML[2][0][h], sML[3][0][h]));
-      const float wi = fast_exp2(sML[tg][0][h] - M);
-      float* dst = sO + (tg * 16 + h) * kDV + 256 * dh + l16;
-#pragma unroll
-      for (int nt = 0; nt < 16; ++nt) dst[16 * nt] = o[nt][i] * wi;
-    }
-  }
-  __syncthreads();
-  // thread -> heads 4(tid/128) .. +3, dims 4(tid % 128) .. +3
-  const int dq = 4 * (tid & 127);
+  float wgt[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int h = 4 * (tid >> 7) + i;
+    const int h = 4 * grp + i;
     float M = kMinusBig;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) M = fmaxf(M, sML[g][0][h]);
+    for (int g = 0; g < kStreams; ++g) M = fmaxf(M, sML[g * 32 + h]);
+    wgt[i] = fast_exp2(sML[tg * 32 + h] - M);
+  }
+  // thread -> dims 4(tid % 64) .. +3 of the half, heads tid / 64 + kWaves j
+  constexpr int kHeadsPerThread = 16 / kWaves;
+  const int dq = 4 * (tid & 63);
+  float Mh[kHeadsPerThread], Lh[kHeadsPerThread];
+#pragma unroll
+  for (int j = 0; j < kHeadsPerThread; ++j) {
+    const int h = (tid >> 6) + kWaves * j;
+    float M = kMinusBig;
+#pragma unroll
+    for (int g = 0; g < kStreams; ++g) M = fmaxf(M, sML[g * 32 + h]);
     float Lsum = 0.0f;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) Lsum += fast_exp2(sML[g][0][h] - M) * sML[g][1][h];
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < kStreams; ++g) Lsum += fast_exp2(sML[g * 32 + h] - M) * sML[g * 32 + 16 + h];
+    Mh[j] = M;
+    Lh[j] = Lsum;
+  }
+  float* const sO = reinterpret_cast<float*>(smem);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) acc += *reinterpret_cast<const f32x4*>(sO + (g * 16 + h) * kDV + dq);
-    if constexpr (DIRECT) {
-      float f = Lsum > 0.0f ? a.out_scale / Lsum : 0.0f;
-      if (Lsum != Lsum) f = Lsum;   // NaN stays NaN
-      *reinterpret_cast<f32x4*>(a.out + ((int64_t)b * H + hbase + h) * kDV + dq) = acc * f;
-      if (a.lse && (tid & 127) == 0)
-        a.lse[(int64_t)b * H + hbase + h] = Lsum > 0.0f ? (M + __log2f(Lsum)) * kLn2 : (Lsum != Lsum ? Lsum : -INFINITY);
-    } else {
-      const int64_t slot = ((int64_t)b * a.num_splits + split) * (H / 16) + hg;
-      *reinterpret_cast<f32x4*>(a.part_o + slot * (16 * kDV) + h * kDV + dq) = acc;
-      if ((tid & 127) == 0) {
-        a.part_ml[slot * 32 + h] = M;
-        a.part_ml[slot * 32 + 16 + h] = Lsum;
+  for (int half = 0; half < 2; ++half) {
+    if (dh == half) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float* dst = sO + (tg * 16 + 4 * grp + i) * kORow + l16;
+#pragma unroll
+        for (int nt = 0; nt < 16; ++nt) dst[16 * nt] = o[nt][i] * wgt[i];
       }
     }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kHeadsPerThread; ++j) {
+      const int h = (tid >> 6) + kWaves * j;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int g = 0; g < kStreams; ++g) acc += *reinterpret_cast<const f32x4*>(sO + (g * 16 + h) * kORow + dq);
+      const int d = 256 * half + dq;
+      if constexpr (DIRECT) {
+        const float Lsum = Lh[j];
+        float f = Lsum > 0.0f ? a.out_scale / Lsum : 0.0f;
+        if (Lsum != Lsum) f = Lsum;   // NaN stays NaN
+        *reinterpret_cast<f32x4*>(a.out + ((int64_t)b * H + hbase + h) * kDV + d) = acc * f;
+        if (a.lse && half == 0 && (tid & 63) == 0)
+          a.lse[(int64_t)b * H + hbase + h] =
+              Lsum > 0.0f ? (Mh[j] + __log2f(Lsum)) * kLn2 : (Lsum != Lsum ? Lsum : -INFINITY);
+      } else {
+        const int64_t slot = ((int64_t)b * a.num_splits + split) * (H / 16) + hg;
+        *reinterpret_cast<f32x4*>(a.part_o + slot * (16 * kDV) + h * kDV + d) = acc;
+        if (half == 0 && (tid & 63) == 0) {
+          a.part_ml[slot * 32 + h] = Mh[j];
+          a.part_ml[slot * 32 + 16 + h] = Lh[j];
+        }
+      }
+    }
+    if (half == 0) __syncthreads();                  // buffer reads done before the second half
   }
 }
 

@@ -7,6 +7,13 @@ namespace mlaq {
 
 enum KvFormat { FMT_BF16 = 0, FMT_FP8 = 1, FMT_NVFP4 = 2 };
 
+// Decode work decomposition, shared by the kernel and the host split planner: a workgroup
+// processes tiles of kDecodeTile tokens, and kDecodeGroupsPerCu workgroups are resident on
+// one CU.
+constexpr int kDecodeTile = 64;
+constexpr int kDecodeGroupsPerCu = 2;
+constexpr int kComputeUnits = 256;
+
 struct DecodeArgs {
   const uint16_t* q;          // bf16 [B, H, 576]
   const uint8_t* kv;          // FP8 [pool, 576] | NVFP4 codes [pool, 288] | BF16 [pool, 576]

@@ -113,7 +113,7 @@ def test_quantize_and_dequantize_validation():
 
 def test_split_planning_and_workspace():
     import synth
-    expect = {"tiny_fp8": 8, "fp8_32k": 32, "nvfp4_32k": 29, "nvfp4_160k": 25, "nvfp4_1m": 128}
+    expect = {"tiny_fp8": 8, "fp8_32k": 64, "nvfp4_32k": 11, "nvfp4_160k": 51, "nvfp4_1m": 256}
     for name, w in synth.WORKLOADS.items():
         p = _p(batch=w.batch, num_heads=w.heads, page_size=w.page_size, max_kv_len=w.kv_len,
                pool_tokens=w.pool_tokens)
