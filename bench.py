@@ -73,28 +73,37 @@ def src_hash() -> str:
 
 
 def timed_steps(step, n_layers, steps, warmup, hip, torch, profile=True):
-    """Run warmup + timed steps; returns (ms per step, split-kernel ms, merge ms)."""
+    """Warmup, then two timed regions of `steps` steps each.  Region 1 launches the steps as
+    they run in use and gives ms per step (the headline).  Region 2 (profile=True) launches
+    the same steps with HIP events recorded at each kernel's own start and end (on the launch
+    stream) and gives the split kernel's and the merge kernel's mean durations.  Returns
+    (ms per step, split-kernel ms, merge ms, ms per step of region 2)."""
     import quantized_kv_paged_amd as qk
     for i in range(warmup):
         step(i % n_layers)
     torch.cuda.synchronize()
-    ev = Events(hip, 4 * steps) if profile else None
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for i in range(steps):
-        if profile:
-            qk.mlaq_set_profile_events(*ev.ev[4 * i:4 * i + 4])
         step(i % n_layers)
     end.record()
     torch.cuda.synchronize()
     total = start.elapsed_time(end) / steps
-    split = merge = None
-    if profile:
-        split = float(np.mean([ev.ms(4 * i, 4 * i + 1) for i in range(steps)]))
-        merges = [m for m in (ev.ms(4 * i + 2, 4 * i + 3) for i in range(steps)) if m is not None]
-        merge = float(np.mean(merges)) if merges else 0.0
-        ev.close()
-    return total, split, merge
+    if not profile:
+        return total, None, None, None
+    ev = Events(hip, 4 * steps)
+    start.record()
+    for i in range(steps):
+        qk.mlaq_set_profile_events(*ev.ev[4 * i:4 * i + 4])
+        step(i % n_layers)
+    end.record()
+    torch.cuda.synchronize()
+    total2 = start.elapsed_time(end) / steps
+    split = float(np.mean([ev.ms(4 * i, 4 * i + 1) for i in range(steps)]))
+    merges = [m for m in (ev.ms(4 * i + 2, 4 * i + 3) for i in range(steps)) if m is not None]
+    merge = float(np.mean(merges)) if merges else 0.0
+    ev.close()
+    return total, split, merge, total2
 
 
 def pmc_traffic(kernel_tag: str, launches_bytes: float):
@@ -198,8 +207,11 @@ def main():
     print(f"[bench] pools ready (host generation {d['gen_s']} s)", file=sys.stderr, flush=True)
 
     p = qk.decode_params(w.batch, w.heads, w.page_size, w.kv_len, w.pool_tokens, w.sm_scale)
-    splits = qk.mlaq_decode_num_splits(p)
-    ws = torch.zeros(max(qk.mlaq_decode_workspace_bytes(p), 256), dtype=torch.uint8, device="cuda")
+    fcode = qk.MLAQ_FP8_E4M3 if fmt == "fp8" else qk.MLAQ_NVFP4
+    splits = qk.mlaq_decode_num_splits(p, fcode)
+    # one workspace large enough for every format run on this shape (the comparison legs)
+    need = max(qk.mlaq_decode_workspace_bytes(p, f) for f in (qk.MLAQ_FP8_E4M3, qk.MLAQ_NVFP4, qk.MLAQ_BF16))
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
     out = torch.empty((w.batch, w.heads, 512), dtype=torch.float32, device="cuda")
     lse = torch.empty((w.batch, w.heads), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream().cuda_stream
@@ -231,7 +243,7 @@ def main():
             step = lambda l: check(L.mla_decode_nvfp4(pp, qp, nvp[l][0], nvp[l][1], 1.0, *common))
         kv_bytes = w.batch * w.kv_len * NV_ROW
 
-    ms, split_ms, merge_ms = timed_steps(step, n_layers, args.steps, args.warmup, hip, torch)
+    ms, split_ms, merge_ms, ms_ev = timed_steps(step, n_layers, args.steps, args.warmup, hip, torch)
     achieved = kv_bytes / (split_ms * 1e-3) / 1e9
     value = kv_bytes / (ms * 1e-3) / 1e9
     kernel_tag = f"mla_decode_kernel_{w.name}"
@@ -247,7 +259,8 @@ def main():
                    "layers_cycled": n_layers, "kv_bytes_per_step": kv_bytes},
         "steps_per_s": round(1000.0 / ms, 1),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
-        "kernels_us": {"split": round(split_ms * 1e3, 2), "merge": round(merge_ms * 1e3, 2)},
+        "kernels_us": {"split": round(split_ms * 1e3, 2), "merge": round(merge_ms * 1e3, 2),
+                       "step_with_kernel_events": round(ms_ev * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": pmc_traffic(kernel_tag, kv_bytes), "kernel": "mla_decode_kernel",
@@ -275,8 +288,9 @@ def main():
         nvs = [(data, scales)] + [(data.clone(), scales.clone()) for _ in range(nl - 1)]
         nvp = [(a.data_ptr(), s.data_ptr()) for a, s in nvs]
         nstep = lambda l: check(L.mla_decode_nvfp4(pp, qp, nvp[l][0], nvp[l][1], 1.0, *common))
-        nms, nsplit, nmerge = timed_steps(nstep, nl, args.steps, args.warmup, hip, torch)
+        nms, nsplit, nmerge, _ = timed_steps(nstep, nl, args.steps, args.warmup, hip, torch)
         res["nvfp4_same_batch"] = {"ms_per_step": round(nms, 5), "steps_per_s": round(1000 / nms, 1),
+                                   "num_splits": qk.mlaq_decode_num_splits(p, qk.MLAQ_NVFP4),
                                    "kv_gbs": round(nv_live / (nms * 1e-3) / 1e9, 1),
                                    "split_kernel_gbs": round(nv_live / (nsplit * 1e-3) / 1e9, 1),
                                    "speedup_vs_fp8": round(ms / nms, 3)}
@@ -289,7 +303,7 @@ def main():
             check(L.kv_dequantize(qk.MLAQ_FP8_E4M3, fp8p[l], None, 1.0, None, w.pool_tokens, w.pool_tokens,
                                   qk.MLAQ_BF16, bf.data_ptr(), stream))
             check(L.mla_decode_bf16(pp, qp, bf.data_ptr(), *common))
-        cms, _, _ = timed_steps(cstep, n_layers, max(20, args.steps // 4), 5, hip, torch, profile=False)
+        cms, _, _, _ = timed_steps(cstep, n_layers, max(20, args.steps // 4), 5, hip, torch, profile=False)
         res["cast_baseline"] = {"ms_per_step": round(cms, 5), "steps_per_s": round(1000 / cms, 1),
                                 "bytes_moved_per_step": w.pool_tokens * (FP8_ROW + BF16_ROW) + w.batch * w.kv_len * BF16_ROW,
                                 "speedup_of_fp8_path": round(cms / ms, 2)}

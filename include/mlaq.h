@@ -84,15 +84,17 @@ typedef struct {            /* (host) */
   float sm_scale;           /* multiplies q . k before the softmax; finite */
 } mlaq_decode_params;
 
-/* (host) Splits the decode will use for these parameters (resolves num_splits = 0), or 0 if
- * the parameters are invalid.  Depends on host arguments only. */
-int32_t mlaq_decode_num_splits(const mlaq_decode_params* p);
+/* (host) Splits a decode of the given KV format (MLAQ_FP8_E4M3, MLAQ_NVFP4 or MLAQ_BF16, the
+ * format of the decode call that will use them) will use for these parameters (resolves
+ * num_splits = 0), or 0 if the parameters or the format are invalid.  The plan depends on
+ * the format because the formats run different workgroup shapes.  Host arguments only. */
+int32_t mlaq_decode_num_splits(const mlaq_decode_params* p, mlaq_format kv_format);
 
-/* (host) Workspace bytes a decode with these parameters needs (0 when it needs none,
+/* (host) Workspace bytes a decode of the given KV format with these parameters needs (0 when it needs none,
  * which is the case for a single split), or SIZE_MAX if the parameters are invalid.
  * The workspace holds one fp32 partial output plus running max and sum per
  * (request, split, 16-head group); it must be 256-byte aligned. */
-size_t mlaq_decode_workspace_bytes(const mlaq_decode_params* p);
+size_t mlaq_decode_workspace_bytes(const mlaq_decode_params* p, mlaq_format kv_format);
 
 /* Decode over an FP8 e4m3fn pool.  kv_scale (> 0, finite) is the per-tensor dequant
  * multiplier: k = e4m3(code) * kv_scale.  Alignment: q, kv, out 16 B; lse 4 B. */

@@ -36,8 +36,8 @@ _lib = ctypes.CDLL(LIB_PATH)
 _vp, _i64, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 _pp = ctypes.POINTER(DecodeParams)
 _SIGS = {
-    "mlaq_decode_num_splits": ([_pp], _i32),
-    "mlaq_decode_workspace_bytes": ([_pp], _sz),
+    "mlaq_decode_num_splits": ([_pp, ctypes.c_int], _i32),
+    "mlaq_decode_workspace_bytes": ([_pp, ctypes.c_int], _sz),
     "mla_decode_fp8": ([_pp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "mla_decode_nvfp4": ([_pp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "mla_decode_bf16": ([_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
@@ -93,19 +93,19 @@ def decode_params(batch, num_heads, page_size, max_kv_len, pool_tokens, sm_scale
     return DecodeParams(batch, num_heads, page_size, max_kv_len, pool_tokens, num_splits, sm_scale)
 
 
-def mlaq_decode_num_splits(p: DecodeParams) -> int:
-    return _lib.mlaq_decode_num_splits(ctypes.byref(p))
+def mlaq_decode_num_splits(p: DecodeParams, kv_format: int) -> int:
+    return _lib.mlaq_decode_num_splits(ctypes.byref(p), kv_format)
 
 
-def mlaq_decode_workspace_bytes(p: DecodeParams) -> int:
-    n = _lib.mlaq_decode_workspace_bytes(ctypes.byref(p))
+def mlaq_decode_workspace_bytes(p: DecodeParams, kv_format: int) -> int:
+    n = _lib.mlaq_decode_workspace_bytes(ctypes.byref(p), kv_format)
     if n == ctypes.c_size_t(-1).value:
         raise MlaqError(2, last_error())
     return n
 
 
-def alloc_workspace(p: DecodeParams, device="cuda") -> torch.Tensor | None:
-    n = mlaq_decode_workspace_bytes(p)
+def alloc_workspace(p: DecodeParams, kv_format: int, device="cuda") -> torch.Tensor | None:
+    n = mlaq_decode_workspace_bytes(p, kv_format)
     return torch.empty(n, dtype=torch.uint8, device=device) if n else None
 
 
@@ -128,7 +128,7 @@ def mla_decode_fp8(q, kv, kv_scale, kv_indptr, kv_indices, kv_lens, page_size, m
     p = _params_for(q, page_size, max_kv_len, kv.shape[0], sm_scale, num_splits)
     out, lse = _decode_outputs(q, out, lse, want_lse)
     if workspace is None:
-        workspace = alloc_workspace(p, q.device)
+        workspace = alloc_workspace(p, MLAQ_FP8_E4M3, q.device)
     _check(_lib.mla_decode_fp8(ctypes.byref(p), _ptr(q), _ptr(kv), kv_scale, _ptr(kv_indptr), _ptr(kv_indices),
                                _ptr(kv_lens), _ptr(out), _ptr(lse), _ptr(workspace),
                                0 if workspace is None else workspace.numel(), _stream(stream)))
@@ -141,7 +141,7 @@ def mla_decode_nvfp4(q, kv_data, kv_scales, global_scale, kv_indptr, kv_indices,
     p = _params_for(q, page_size, max_kv_len, kv_data.shape[0], sm_scale, num_splits)
     out, lse = _decode_outputs(q, out, lse, want_lse)
     if workspace is None:
-        workspace = alloc_workspace(p, q.device)
+        workspace = alloc_workspace(p, MLAQ_NVFP4, q.device)
     _check(_lib.mla_decode_nvfp4(ctypes.byref(p), _ptr(q), _ptr(kv_data), _ptr(kv_scales), global_scale,
                                  _ptr(kv_indptr), _ptr(kv_indices), _ptr(kv_lens), _ptr(out), _ptr(lse),
                                  _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream)))
@@ -154,7 +154,7 @@ def mla_decode_bf16(q, kv, kv_indptr, kv_indices, kv_lens, page_size, max_kv_len
     p = _params_for(q, page_size, max_kv_len, kv.shape[0], sm_scale, num_splits)
     out, lse = _decode_outputs(q, out, lse, want_lse)
     if workspace is None:
-        workspace = alloc_workspace(p, q.device)
+        workspace = alloc_workspace(p, MLAQ_BF16, q.device)
     _check(_lib.mla_decode_bf16(ctypes.byref(p), _ptr(q), _ptr(kv), _ptr(kv_indptr), _ptr(kv_indices),
                                 _ptr(kv_lens), _ptr(out), _ptr(lse), _ptr(workspace),
                                 0 if workspace is None else workspace.numel(), _stream(stream)))

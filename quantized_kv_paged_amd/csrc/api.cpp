@@ -28,15 +28,17 @@ mlaq_status fail(mlaq_status s, const char* fmt, ...) {
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
 
-constexpr int kTileTokens = mlaq::kDecodeTile;   // tokens per decode tile
-constexpr int kResidentSlots = mlaq::kComputeUnits * mlaq::kDecodeGroupsPerCu;   // resident decode workgroups
 
-// Split planning.  Every workgroup processes one (request, chunk, 16-head group); with all
-// requests at the host-known bound, workgroups run in "rounds" of kResidentSlots.  The cost
-// (in tile-times) is rounds * (tiles per chunk + fixed per-workgroup cost) plus the partial
-// write + merge read, and the smallest-cost split count is taken (ties -> fewer splits).
-int plan_splits(int batch, int head_groups, int max_kv_len) {
-  const int tiles = (max_kv_len + kTileTokens - 1) / kTileTokens;
+// Split planning.  Every workgroup processes one (request, chunk, 16-head group) in tiles of
+// the format's tile size; with all requests at the host-known bound, workgroups run in
+// "rounds" of the resident slots (CUs x workgroups per CU).  The cost (in tile-times) is
+// rounds * (tiles per chunk + fixed per-workgroup cost) plus the partial write + merge read,
+// and the smallest-cost split count is taken (ties -> fewer splits).
+int plan_splits(int fmt, int batch, int head_groups, int max_kv_len) {
+  const int streams = mlaq::decode_streams(fmt);
+  const int tile = mlaq::decode_tile(streams);
+  const double slots = (double)mlaq::kComputeUnits * mlaq::decode_groups_per_cu(streams);
+  const int tiles = (max_kv_len + tile - 1) / tile;
   if (tiles <= 1 || batch <= 0) return 1;
   const double fixed = 0.5, merge = 0.5;
   int best = 1;
@@ -44,9 +46,9 @@ int plan_splits(int batch, int head_groups, int max_kv_len) {
   const int smax = tiles < MLAQ_MAX_SPLITS ? tiles : MLAQ_MAX_SPLITS;
   for (int s = 1; s <= smax; ++s) {
     const double wgs = (double)batch * head_groups * s;
-    const double rounds = std::ceil(wgs / kResidentSlots);
+    const double rounds = std::ceil(wgs / slots);
     const double per = std::ceil((double)tiles / s);
-    const double cost = rounds * (per + fixed) + (s > 1 ? merge * wgs / kResidentSlots : 0.0);
+    const double cost = rounds * (per + fixed) + (s > 1 ? merge * wgs / slots : 0.0);
     if (cost < best_cost - 1e-9) { best_cost = cost; best = s; }
   }
   return best;
@@ -69,8 +71,13 @@ mlaq_status check_params(const mlaq_decode_params* p) {
   return MLAQ_OK;
 }
 
-int resolve_splits(const mlaq_decode_params* p) {
-  return p->num_splits > 0 ? p->num_splits : plan_splits(p->batch, p->num_heads / 16, p->max_kv_len);
+int resolve_splits(int fmt, const mlaq_decode_params* p) {
+  return p->num_splits > 0 ? p->num_splits : plan_splits(fmt, p->batch, p->num_heads / 16, p->max_kv_len);
+}
+
+// mlaq_format of a decode's KV pool -> kernel format; -1 if it is not a decode format
+int kv_format_of(mlaq_format f) {
+  return f == MLAQ_FP8_E4M3 ? mlaq::FMT_FP8 : f == MLAQ_NVFP4 ? mlaq::FMT_NVFP4 : f == MLAQ_BF16 ? mlaq::FMT_BF16 : -1;
 }
 
 size_t workspace_for(const mlaq_decode_params* p, int splits) {
@@ -98,7 +105,7 @@ mlaq_status decode_common(int fmt, const mlaq_decode_params* p, const uint16_t* 
     return fail(MLAQ_ERR_ALIGN, "kv_indptr, kv_indices and kv_lens must be 4-byte aligned");
   if (fmt != mlaq::FMT_BF16 && !finite_pos(scale))
     return fail(MLAQ_ERR_VALUE, "the KV scale must be finite and > 0 (got %g)", (double)scale);
-  const int splits = resolve_splits(p);
+  const int splits = resolve_splits(fmt, p);
   const size_t need = workspace_for(p, splits);
   if (need > 0) {
     if (!workspace) return fail(MLAQ_ERR_NULL, "workspace is NULL but %zu bytes are needed", need);
@@ -106,7 +113,8 @@ mlaq_status decode_common(int fmt, const mlaq_decode_params* p, const uint16_t* 
       return fail(MLAQ_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
     if (!aligned(workspace, 256)) return fail(MLAQ_ERR_ALIGN, "workspace must be 256-byte aligned");
   }
-  const int tiles = (p->max_kv_len + kTileTokens - 1) / kTileTokens;
+  const int tile = mlaq::decode_tile(mlaq::decode_streams(fmt));
+  const int tiles = (p->max_kv_len + tile - 1) / tile;
   const int per = (tiles + splits - 1) / splits;
 
   mlaq::DecodeArgs a;
@@ -128,7 +136,7 @@ mlaq_status decode_common(int fmt, const mlaq_decode_params* p, const uint16_t* 
   a.page_shift = __builtin_ctz((unsigned)p->page_size);
   a.max_kv_len = p->max_kv_len;
   a.num_splits = splits;
-  a.chunk_tokens = (per > 0 ? per : 1) * kTileTokens;
+  a.chunk_tokens = (per > 0 ? per : 1) * tile;
   const float s = fmt == mlaq::FMT_BF16 ? 1.0f : scale;
   a.score_scale = p->sm_scale * s * 1.4426950408889634f;
   a.out_scale = s;
@@ -156,14 +164,18 @@ mlaq_status mlaq_set_profile_events(hipEvent_t split_start, hipEvent_t split_end
   return MLAQ_OK;
 }
 
-int32_t mlaq_decode_num_splits(const mlaq_decode_params* p) {
+int32_t mlaq_decode_num_splits(const mlaq_decode_params* p, mlaq_format kv_format) {
+  const int fmt = kv_format_of(kv_format);
+  if (fmt < 0) { fail(MLAQ_ERR_UNSUPPORTED, "kv_format %d is not a decode KV format", (int)kv_format); return 0; }
   if (check_params(p) != MLAQ_OK) return 0;
-  return resolve_splits(p);
+  return resolve_splits(fmt, p);
 }
 
-size_t mlaq_decode_workspace_bytes(const mlaq_decode_params* p) {
+size_t mlaq_decode_workspace_bytes(const mlaq_decode_params* p, mlaq_format kv_format) {
+  const int fmt = kv_format_of(kv_format);
+  if (fmt < 0) { fail(MLAQ_ERR_UNSUPPORTED, "kv_format %d is not a decode KV format", (int)kv_format); return SIZE_MAX; }
   if (check_params(p) != MLAQ_OK) return SIZE_MAX;
-  return workspace_for(p, resolve_splits(p));
+  return workspace_for(p, resolve_splits(fmt, p));
 }
 
 mlaq_status mla_decode_fp8(const mlaq_decode_params* p, const uint16_t* q, const uint8_t* kv, float kv_scale,

@@ -46,21 +46,26 @@
 
 namespace mlaq {
 
-constexpr int kStreams = 2;                // online-softmax streams (token groups) per workgroup
 constexpr int kBlocks = 2;                 // 16-token MFMA blocks per wave per tile
-constexpr int kTile = 16 * kBlocks * kStreams;   // tokens per tile
-constexpr int kWaves = 2 * kStreams;       // (token group, dim half) pairs
-constexpr int kThreads = 64 * kWaves;
-static_assert(kTile == kDecodeTile, "tile size shared with the host planner");
 constexpr int kVRow = 512;                 // bytes per LDS value row of a wave (its 256 fp16 dims)
 constexpr int kWaveV = 16 * kBlocks * kVRow;       // a wave's value tile (16 KB)
 constexpr int kSwapW = kBlocks * 64 * 16;          // bytes of a wave's partial scores (2 KB)
-constexpr int kSwap = kWaves * kWaveV;             // byte offset of the swap buffers [2][kWaves]
-constexpr int kSmem = kSwap + 2 * kWaves * kSwapW; // 80 KB: two workgroups share a CU
 constexpr int kORow = 260;                 // fp32 row stride of the end-of-chunk merge buffer (padded)
-constexpr int kMLOff = kSmem - kStreams * 2 * 16 * 4;   // byte offset of the streams' (m, l)
-static_assert(kStreams * 16 * kORow * 4 <= kMLOff, "merge buffer overlaps the (m, l) table");
-static_assert(2 * kSmem <= 160 * 1024, "two workgroups per CU");
+
+// Workgroup geometry for NS online-softmax streams (token groups): 2 NS waves (one per
+// (stream, dim half)), tiles of 32 NS tokens, LDS = value tiles + double-buffered score swap.
+template <int NS> struct Geo {
+  static constexpr int kStreams = NS;
+  static constexpr int kTile = 16 * kBlocks * NS;
+  static constexpr int kWaves = 2 * NS;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kSwap = kWaves * kWaveV;                 // byte offset of the swap buffers
+  static constexpr int kSmem = kSwap + 2 * kWaves * kSwapW;     // 40 KB (NS = 1) or 80 KB (NS = 2)
+  static constexpr int kMLOff = kSmem - NS * 2 * 16 * 4;        // byte offset of the streams' (m, l)
+  static_assert(NS * 16 * kORow * 4 <= kMLOff, "merge buffer overlaps the (m, l) table");
+  static_assert(kTile == decode_tile(NS), "tile size shared with the host planner");
+  static_assert(decode_groups_per_cu(NS) * kSmem <= 160 * 1024, "resident workgroups per CU");
+};
 constexpr float kMinusBig = -3.0e38f;   // initial running max: finite, so an empty stream stays finite
 constexpr float kSlack = 8.0f;          // lazy-rescale threshold of the running max (log2 units)
 
@@ -266,8 +271,11 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-template <int FMT, bool DIRECT, bool TILEPAGE>
-__global__ __launch_bounds__(kThreads, 2) void mla_decode_kernel(DecodeArgs a) {
+template <int FMT, bool DIRECT, bool TILEPAGE, int NS>
+__global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(DecodeArgs a) {
+  constexpr int kStreams = Geo<NS>::kStreams, kTile = Geo<NS>::kTile, kWaves = Geo<NS>::kWaves;
+  constexpr int kThreads = Geo<NS>::kThreads, kSwap = Geo<NS>::kSwap, kSmem = Geo<NS>::kSmem;
+  constexpr int kMLOff = Geo<NS>::kMLOff;
   typedef typename OpType<FMT>::type Op;
   // raw tiles in flight per wave: two for the 8-bit and 4-bit pools, one for the 16-bit pool
   constexpr int kBufs = 1;
@@ -703,22 +711,25 @@ static hipError_t launch(K kernel, dim3 grid, dim3 block, hipStream_t stream, hi
   return hipGetLastError();
 }
 
-template <int FMT, bool TILEPAGE>
+template <int FMT, bool TILEPAGE, int NS>
 static hipError_t launch_fmt(const DecodeArgs& a, hipStream_t stream, const ProfileEvents& ev) {
-  const dim3 grid(a.num_splits, a.batch, a.num_heads / 16);
+  const dim3 grid(a.num_splits, a.batch, a.num_heads / 16), block(Geo<NS>::kThreads);
   if (a.num_splits == 1)
-    return launch(mla_decode_kernel<FMT, true, TILEPAGE>, grid, dim3(kThreads), stream, ev.split_start,
-                  ev.split_end, a);
-  hipError_t e = launch(mla_decode_kernel<FMT, false, TILEPAGE>, grid, dim3(kThreads), stream, ev.split_start,
+    return launch(mla_decode_kernel<FMT, true, TILEPAGE, NS>, grid, block, stream, ev.split_start, ev.split_end, a);
+  hipError_t e = launch(mla_decode_kernel<FMT, false, TILEPAGE, NS>, grid, block, stream, ev.split_start,
                         ev.split_end, a);
   if (e != hipSuccess) return e;
   return launch(mla_merge_kernel, dim3(2, a.num_heads, a.batch), dim3(kMergeThreads), stream, ev.merge_start,
                 ev.merge_end, a);
 }
 
+// Pages of at least a tile hold whole tiles (one descriptor per tile); shorter pages are
+// read row by row.
 template <int FMT>
 static hipError_t launch_pages(const DecodeArgs& a, hipStream_t stream, const ProfileEvents& ev) {
-  return a.page_size >= kTile ? launch_fmt<FMT, true>(a, stream, ev) : launch_fmt<FMT, false>(a, stream, ev);
+  constexpr int NS = decode_streams(FMT);
+  return a.page_size >= Geo<NS>::kTile ? launch_fmt<FMT, true, NS>(a, stream, ev)
+                                       : launch_fmt<FMT, false, NS>(a, stream, ev);
 }
 
 hipError_t launch_decode(int fmt, const DecodeArgs& a, hipStream_t stream, const ProfileEvents& ev) {

@@ -7,11 +7,16 @@ namespace mlaq {
 
 enum KvFormat { FMT_BF16 = 0, FMT_FP8 = 1, FMT_NVFP4 = 2 };
 
-// Decode work decomposition, shared by the kernel and the host split planner: a workgroup
-// processes tiles of kDecodeTile tokens, and kDecodeGroupsPerCu workgroups are resident on
-// one CU.
-constexpr int kDecodeTile = 64;
-constexpr int kDecodeGroupsPerCu = 2;
+// Decode work decomposition, shared by the kernel and the host split planner.  A workgroup
+// runs `streams` online-softmax streams of 32 tokens per tile (2 waves per stream), and
+// 160 KB of LDS holds 4 / streams workgroups per CU.  NVFP4 tiles are bound by the
+// conversion arithmetic and the per-tile chain of the wave pair, so they take single-stream
+// workgroups, whose barrier covers only the pair that swaps scores; FP8 and BF16 tiles carry
+// two to four times the bytes per token, so they take two-stream workgroups, which halve the
+// split partials.
+constexpr int decode_streams(int fmt) { return fmt == FMT_NVFP4 ? 1 : 2; }
+constexpr int decode_tile(int streams) { return 32 * streams; }
+constexpr int decode_groups_per_cu(int streams) { return 4 / streams; }
 constexpr int kComputeUnits = 256;
 
 struct DecodeArgs {

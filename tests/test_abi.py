@@ -75,7 +75,7 @@ def test_pointer_and_value_validation():
     assert _fp8(p, scale=0.0) == ERR_VALUE
     assert _fp8(p, scale=float("inf")) == ERR_VALUE
     assert _fp8(p, ws=None) == ERR_NULL
-    need = qk.mlaq_decode_workspace_bytes(p)
+    need = qk.mlaq_decode_workspace_bytes(p, qk.MLAQ_FP8_E4M3)
     assert need > 0
     assert _fp8(p, ws_bytes=need - 1) == ERR_WORKSPACE
     assert _fp8(p, ws=FAKE + 16) == ERR_ALIGN
@@ -113,18 +113,27 @@ def test_quantize_and_dequantize_validation():
 
 def test_split_planning_and_workspace():
     import synth
-    expect = {"tiny_fp8": 8, "fp8_32k": 64, "nvfp4_32k": 11, "nvfp4_160k": 51, "nvfp4_1m": 256}
+    # (FP8 plan, NVFP4 plan): FP8 workgroups stream 64-token tiles, two per CU; NVFP4
+    # workgroups stream 32-token tiles, four per CU
+    expect = {"tiny_fp8": (8, 16), "fp8_32k": (64, 128), "nvfp4_32k": (11, 23), "nvfp4_160k": (51, 101),
+              "nvfp4_1m": (256, 512)}
     for name, w in synth.WORKLOADS.items():
         p = _p(batch=w.batch, num_heads=w.heads, page_size=w.page_size, max_kv_len=w.kv_len,
                pool_tokens=w.pool_tokens)
-        s = qk.mlaq_decode_num_splits(p)
-        assert s == expect[name], (name, s)
-        ws = qk.mlaq_decode_workspace_bytes(p)
-        slots = w.batch * s * (w.heads // 16)
-        assert ws == ((slots * (16 * 512 * 4 + 32 * 4) + 255) // 256) * 256
-    assert qk.mlaq_decode_num_splits(_p(max_kv_len=64)) == 1
-    assert qk.mlaq_decode_workspace_bytes(_p(max_kv_len=64)) == 0
-    assert qk.mlaq_decode_num_splits(_p(num_splits=7)) == 7
-    assert qk.mlaq_decode_num_splits(_p(num_heads=20)) == 0
+        for fmt, want in zip((qk.MLAQ_FP8_E4M3, qk.MLAQ_NVFP4), expect[name]):
+            s = qk.mlaq_decode_num_splits(p, fmt)
+            assert s == want, (name, fmt, s)
+            ws = qk.mlaq_decode_workspace_bytes(p, fmt)
+            slots = w.batch * s * (w.heads // 16)
+            assert ws == ((slots * (16 * 512 * 4 + 32 * 4) + 255) // 256) * 256
+        assert qk.mlaq_decode_num_splits(p, qk.MLAQ_BF16) == expect[name][0]
+    for fmt in (qk.MLAQ_FP8_E4M3, qk.MLAQ_NVFP4, qk.MLAQ_BF16):
+        assert qk.mlaq_decode_num_splits(_p(max_kv_len=32), fmt) == 1
+        assert qk.mlaq_decode_workspace_bytes(_p(max_kv_len=32), fmt) == 0
+        assert qk.mlaq_decode_num_splits(_p(num_splits=7), fmt) == 7
+        assert qk.mlaq_decode_num_splits(_p(num_heads=20), fmt) == 0
+        with pytest.raises(MlaqError):
+            qk.mlaq_decode_workspace_bytes(_p(num_heads=20), fmt)
+    assert qk.mlaq_decode_num_splits(_p(), qk.MLAQ_FP32) == 0          # not a decode KV format
     with pytest.raises(MlaqError):
-        qk.mlaq_decode_workspace_bytes(_p(num_heads=20))
+        qk.mlaq_decode_workspace_bytes(_p(), qk.MLAQ_FP32)

@@ -89,9 +89,13 @@ def test_page_placement_is_bitwise_invariant():
         assert np.array_equal(o1, o2) and np.array_equal(l1, l2), s
 
 
-def test_fp8_and_nvfp4_bitwise_equal_on_shared_values():
+def test_fp8_and_nvfp4_agree_on_shared_values():
     """An FP8 pool and an NVFP4 pool (all block scales 1.0, global scale 1.0) holding the same
-    E2M1 values dequantize to the same fp16 operands, so the two decodes agree bit for bit."""
+    E2M1 values dequantize to the same fp16 operands.  The two formats run different workgroup
+    shapes (two softmax streams per workgroup for FP8, one for NVFP4), so probabilities are
+    rounded to fp16 against different running maxima and sums are grouped differently: the
+    outputs must agree to that rounding (about 2^-11 relative), far inside the oracle
+    tolerance."""
     c = build_case("fp8", [333, 1024], 64, seed=22)
     rng = np.random.default_rng(6)
     codes = rng.integers(0, 16, size=c.fp8_pool.shape, dtype=np.uint8)
@@ -106,7 +110,8 @@ def test_fp8_and_nvfp4_bitwise_equal_on_shared_values():
     for s in (0, 1):
         o1, l1 = gpu_decode(c, Device(c), num_splits=s)
         o2, l2 = gpu_decode(nv, Device(nv), num_splits=s)
-        assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+        assert np.abs(o1 - o2).max() <= 1e-3 * max(1.0, np.abs(o1).max()), s
+        assert np.abs(l1 - l2).max() <= 1e-4, s
     ref_out, ref_lse = oracle_decode(nv)
     assert_parity(o2, l2, ref_out, ref_lse, tag="shared values")
 

@@ -46,7 +46,8 @@ def _setup(name):
     d = dict(q=_dev(synth.q_bits(w.seed, w.batch, w.heads).view(np.int16)).view(torch.bfloat16),
              indptr=_dev(pt.kv_indptr), indices=_dev(pt.kv_indices), lens=_dev(pt.kv_lens))
     p = qk.decode_params(w.batch, w.heads, w.page_size, w.kv_len, w.pool_tokens, w.sm_scale)
-    print(f"[{name}] pool {host.shape}, {qk.mlaq_decode_num_splits(p)} splits", flush=True)
+    fmt = qk.MLAQ_NVFP4 if w.fmt == "nvfp4" else qk.MLAQ_FP8_E4M3
+    print(f"[{name}] pool {host.shape}, {qk.mlaq_decode_num_splits(p, fmt)} splits", flush=True)
     return qk, w, pt, host, d
 
 
