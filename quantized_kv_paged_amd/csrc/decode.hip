@@ -69,13 +69,16 @@ template <int NS> struct Geo {
 constexpr float kMinusBig = -3.0e38f;   // initial running max: finite, so an empty stream stays finite
 constexpr float kSlack = 8.0f;          // lazy-rescale threshold of the running max (log2 units)
 
-// The lane's share of one token row for its dim half dh and lane group g:
-//   k-block kb < 8 (m = kb/2, h = kb%2): value dims 256dh + 64m + 16g + 8h .. +8;  kb = 8:
-//   rope dims 512 + 32dh + 8g .. +8.  (Any order of the 576 dims gives the same dot product;
-//   the query operand uses the same map.)
+// The lane's share of one token row for its dim half dh and lane group g, as 9 k-blocks of 8
+// dims (any order of the 576 dims gives the same dot product; the query operand uses the same
+// map).  The map is chosen per format so that a lane's k-blocks are 16 contiguous bytes of
+// the row and the four lane groups of a token read 64 contiguous bytes:
+//   FP8, BF16: kb < 8 (m = kb/2, h = kb%2): value dims 256dh + 64m + 16g + 8h .. +8
+//   NVFP4:     kb < 8 (c = kb/4, s = kb%4): value dims 256dh + 128c + 32g + 8s .. +8
+//   kb = 8: rope dims 512 + 32dh + 8g .. +8.
 template <int FMT> struct RawTile;
 template <> struct RawTile<FMT_FP8> { u32x4 d[4]; u32x2 e; };                  // 4 x 16 B + 8 B
-template <> struct RawTile<FMT_NVFP4> { u32x2 d[4]; uint32_t e; uint32_t s[5]; };  // codes + scales
+template <> struct RawTile<FMT_NVFP4> { u32x4 d[2]; uint32_t e; uint32_t s[5]; };  // codes + scales
 template <> struct RawTile<FMT_BF16> { u32x4 d[9]; };                           // 9 x 16 B
 
 template <int FMT> struct OpType { typedef f16x8 type; typedef _Float16 elem; };
@@ -90,8 +93,11 @@ template <> struct OpType<FMT_BF16> { typedef bf16x8 type; typedef __bf16 elem; 
 // per-lane base XOR a per-instruction constant in bits 4-7, plus a constant offset.
 __device__ __forceinline__ int vswz(int r) { const int x = r & 15; return (x ^ (x << 1)) & 15; }
 
+template <int FMT>
 __device__ __forceinline__ int kb_dim(int dh, int kb, int g) {
-  return kb < 8 ? 256 * dh + 64 * (kb >> 1) + 16 * g + 8 * (kb & 1) : 512 + 32 * dh + 8 * g;
+  if (kb == 8) return 512 + 32 * dh + 8 * g;
+  return FMT == FMT_NVFP4 ? 256 * dh + 128 * (kb >> 2) + 32 * g + 8 * (kb & 3)
+                          : 256 * dh + 64 * (kb >> 1) + 16 * g + 8 * (kb & 1);
 }
 
 // The chunk's page-table entries, 64 at a time: lane l of `cur` holds entry
@@ -146,7 +152,7 @@ __device__ __forceinline__ void load_raw(RawTile<FMT>& r, const DecodeArgs& a, i
   } else if constexpr (FMT == FMT_NVFP4) {
     const uint8_t* base = a.kv + row * kNvData;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) r.d[m] = *reinterpret_cast<const u32x2*>(base + 128 * dh + 32 * m + 8 * g);
+    for (int c = 0; c < 2; ++c) r.d[c] = *reinterpret_cast<const u32x4*>(base + 128 * dh + 64 * c + 16 * g);
     r.e = *reinterpret_cast<const uint32_t*>(base + 256 + 16 * dh + 4 * g);
     const uint32_t* sp = reinterpret_cast<const uint32_t*>(a.kv_scales + row * kNvScale);
     const u32x4 s4 = *reinterpret_cast<const u32x4_a4*>(sp + 4 * dh);   // blocks 16dh .. 16dh+15
@@ -176,7 +182,7 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int tok_in_tile, int dh, int
     o.e = tok_in_tile * kD + 512 + 32 * dh + 8 * g;
     o.s = 0;
   } else if constexpr (FMT == FMT_NVFP4) {
-    o.v = tok_in_tile * kNvData + 128 * dh + 8 * g;
+    o.v = tok_in_tile * kNvData + 128 * dh + 16 * g;
     o.e = tok_in_tile * kNvData + 256 + 16 * dh + 4 * g;
     o.s = tok_in_tile * kNvScale + 16 * dh;
   } else {
@@ -198,7 +204,7 @@ __device__ __forceinline__ void load_raw_tile(RawTile<FMT>& r, BufferRsrc kv, Bu
   } else if constexpr (FMT == FMT_NVFP4) {
     const uint32_t so = tok0 * kNvData, ss = tok0 * kNvScale;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) r.d[m] = buffer_load_b64(kv, o.v + 32 * m, so);
+    for (int c = 0; c < 2; ++c) r.d[c] = buffer_load_b128(kv, o.v + 64 * c, so);
     r.e = buffer_load_b32(kv, o.e, so);
     const u32x4 s4 = buffer_load_b128(sc, o.s, ss);          // blocks 16dh .. 16dh+15
     r.s[0] = s4[0]; r.s[1] = s4[1]; r.s[2] = s4[2]; r.s[3] = s4[3];
@@ -228,7 +234,9 @@ __device__ __forceinline__ void fix_raw(RawTile<FMT>& r, int state) {
   } else if constexpr (FMT == FMT_NVFP4) {
     const uint32_t f = state == 2 ? 0x7f7f7f7fu : 0u;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) { r.d[m][0] = state ? 0u : r.d[m][0]; r.d[m][1] = state ? 0u : r.d[m][1]; }
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r.d[c][e] = state ? 0u : r.d[c][e];
     r.e = state ? 0u : r.e;
 #pragma unroll
     for (int k = 0; k < 5; ++k) r.s[k] = state ? f : r.s[k];
@@ -241,9 +249,10 @@ __device__ __forceinline__ void fix_raw(RawTile<FMT>& r, int state) {
   }
 }
 
-// MFMA operand of k-block KB of the lane's row half.  NVFP4: the 16-dim block of k-block
-// 2m + h is byte g of s[m] (selector ssel[0]), that of k-block 8 byte 2dh + g/2 of s[4]
-// (ssel[1]); each selector also replicates the byte into both halves of the fp16 pair.
+// MFMA operand of k-block KB of the lane's row half.  NVFP4: the 16-dim blocks of k-blocks
+// 4c + s are bytes 2g (s < 2) and 2g + 1 (s >= 2) of the dword pair (s[2c], s[2c + 1]);
+// selector ssel[0] picks both, each replicated into the two halves of an fp16 pair; the
+// block of k-block 8 is byte 2dh + g/2 of s[4] (selector ssel[1]).
 template <int FMT, int KB>
 __device__ __forceinline__ typename OpType<FMT>::type dequant(const RawTile<FMT>& r, const uint32_t* ssel) {
   if constexpr (FMT == FMT_FP8) {
@@ -253,10 +262,14 @@ __device__ __forceinline__ typename OpType<FMT>::type dequant(const RawTile<FMT>
     const f16x2 c = fp8x2_to_f16<false>(w1), d = fp8x2_to_f16<true>(w1);
     return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
   } else if constexpr (FMT == FMT_NVFP4) {
-    const uint32_t sb = KB < 8 ? __builtin_amdgcn_perm(0u, r.s[KB >> 1], ssel[0])
-                               : __builtin_amdgcn_perm(0u, r.s[4], ssel[1]);
-    const f16x2 s2 = fp8x2_to_f16<false>(sb);
-    const uint32_t w = KB < 8 ? r.d[KB >> 1][KB & 1] : r.e;
+    f16x2 s2;
+    if constexpr (KB < 8) {
+      const uint32_t sb = __builtin_amdgcn_perm(r.s[2 * (KB >> 2) + 1], r.s[2 * (KB >> 2)], ssel[0]);
+      s2 = fp8x2_to_f16<((KB & 3) >= 2)>(sb);
+    } else {
+      s2 = fp8x2_to_f16<false>(__builtin_amdgcn_perm(0u, r.s[4], ssel[1]));
+    }
+    const uint32_t w = KB < 8 ? r.d[KB >> 2][KB & 3] : r.e;
     const f16x2 a = fp4x2_to_f16<0>(w) * s2, b = fp4x2_to_f16<1>(w) * s2;
     const f16x2 c = fp4x2_to_f16<2>(w) * s2, d = fp4x2_to_f16<3>(w) * s2;
     return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
@@ -368,7 +381,7 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
   {
     const uint16_t* qrow = a.q + ((int64_t)b * H + hbase + l16) * kD;
 #pragma unroll
-    for (int kb = 0; kb < 9; ++kb) qraw[kb] = *reinterpret_cast<const u32x4*>(qrow + kb_dim(dh, kb, grp));
+    for (int kb = 0; kb < 9; ++kb) qraw[kb] = *reinterpret_cast<const u32x4*>(qrow + kb_dim<FMT>(dh, kb, grp));
   }
   fetch(rawA, stA, t_begin);
   if constexpr (kBufs == 2) {
@@ -413,17 +426,19 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
   // NVFP4 block-scale byte selectors (see dequant)
   uint32_t ssel[2];
   {
-    const uint32_t b0 = (uint32_t)grp, b1 = (uint32_t)(2 * dh + (grp >> 1));
-    ssel[0] = b0 | (b0 << 8) | 0x0c0c0000u;
+    const uint32_t b0 = 2u * grp, b1 = (uint32_t)(2 * dh + (grp >> 1));
+    ssel[0] = b0 | (b0 << 8) | ((b0 + 1) << 16) | ((b0 + 1) << 24);
     ssel[1] = b1 | (b1 << 8) | 0x0c0c0000u;
   }
   // Byte addresses in the wave's value tile (rows = its 32 tokens 16tb + r, dims relative to
-  // 256dh).  Writes of k-block 2m + h of block tb: row 16tb + l16, chunk
-  // 16(m >> 1) + ((8(m & 1) | 2g | h) ^ vswz(l16)), i.e. vwb ^ 16(8(m & 1) | h), plus
-  // 256(m >> 1) + 16 kVRow tb.  Transposed reads of dims 16nt + 4q .. +3 of block tb by lane
+  // 256dh).  Writes of k-block kb of block tb: row 16tb + l16, chunk kb_dim / 8 stored at its
+  // bits 0-3 XOR vswz(l16): FP8 / BF16 chunk 16(m >> 1) + (8(m & 1) | 2g | h) for kb = 2m + h,
+  // i.e. vwb ^ 16(8(m & 1) | h), plus 256(m >> 1); NVFP4 chunk 16c + (4g | s) for kb = 4c + s,
+  // i.e. vwb ^ 16s, plus 256c; plus 16 kVRow tb.  (Both write patterns and the reads below are
+  // conflict-free, checked by enumeration.)  Transposed reads of dims 16nt + 4q .. +3 of block tb by lane
   // (g, 4i + q): row 16tb + 4g + i, chunk 16(nt >> 3) + ((2(nt & 7) | (q >> 1)) ^ vswz(row)),
   // i.e. vrb ^ 32(nt & 7), plus 256(nt >> 3) + 16 kVRow tb.
-  const int vwb = l16 * kVRow + 16 * ((2 * grp) ^ vswz(l16));
+  const int vwb = l16 * kVRow + 16 * (((FMT == FMT_NVFP4 ? 4 : 2) * grp) ^ vswz(l16));
   const int q4 = l16 & 3, vrow = 4 * grp + (l16 >> 2);
   const int vrb = vrow * kVRow + 16 * ((q4 >> 1) ^ vswz(vrow)) + 8 * (q4 & 1);
 
@@ -443,8 +458,8 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
       const Op kop = dequant<FMT, KB>(cur[tb], ssel);                                             \
       sacc[tb] = mfma16x16x32(kop, qop[KB], sacc[tb]);                                            \
       if (KB < 8)                                                                                 \
-        *reinterpret_cast<Op*>(vt + ((vwb ^ (16 * ((KB & 2) * 4 + (KB & 1)))) + 256 * (KB >> 2) + \
-                                     16 * kVRow * tb)) = kop;                                     \
+        *reinterpret_cast<Op*>(vt + ((vwb ^ (16 * (FMT == FMT_NVFP4 ? (KB & 3) : (KB & 2) * 4 + (KB & 1)))) + \
+                                     256 * (KB >> 2) + 16 * kVRow * tb)) = kop;                   \
     }
     MLAQ_QK_STEP(0) MLAQ_QK_STEP(1) MLAQ_QK_STEP(2) MLAQ_QK_STEP(3) MLAQ_QK_STEP(4)
     MLAQ_QK_STEP(5) MLAQ_QK_STEP(6) MLAQ_QK_STEP(7) MLAQ_QK_STEP(8)
