@@ -636,39 +636,46 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
   }
 }
 
-// Merge of the split partials of one (request, head, 256-dim half) by 4 waves: weights
+// Merge of the split partials of one (request, head, DIMS-dim chunk): weights
 // w_s = 2^(m_s - M) over the splits (M = max_s m_s), output = sum_s w_s O_s / sum_s w_s l_s,
-// natural-log lse.  Wave w sums splits s = w (mod 4); each lane holds 4 dims.  The partial
-// loads of the first 32 splits are issued before the weights are computed, so their latency
-// overlaps that of the (m, l) loads and the reductions.
+// natural-log lse.  The 256 threads are 1024 / DIMS groups of DIMS / 4 lanes; group k sums the
+// splits s = k (mod groups), each lane 4 dims, so every load of a group is DIMS x 4 contiguous
+// bytes.  Narrow chunks (DIMS = 64) spread small batches over many workgroups; wide ones
+// (DIMS = 256) keep large batches from repeating the weight computation.  The partial loads
+// of the first splits are issued before the weights are computed, so their latency overlaps
+// that of the (m, l) loads and the reductions.
 constexpr int kMergeThreads = 256;
-constexpr int kMergeUnroll = 8;   // splits per wave per batch of loads
+constexpr int kMergeUnroll = 4;                                  // splits per group per batch of loads
+template <int DIMS>
 __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(DecodeArgs a) {
+  constexpr int kMergeDims = DIMS;                                 // dims per workgroup
+  constexpr int kMergeGroups = kMergeThreads / (kMergeDims / 4);   // split-strided lane groups
   __shared__ float sw[MLAQ_MAX_SPLITS];
-  __shared__ __attribute__((aligned(16))) float sred[4][256];
+  __shared__ __attribute__((aligned(16))) float sred[kMergeGroups][kMergeDims];
   __shared__ float sx[2][4];
-  const int half = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int grp = tid / (kMergeDims / 4), li = tid % (kMergeDims / 4);
   const int H = a.num_heads, hg = h >> 4, hh = h & 15, S = a.num_splits, HG = H / 16;
   const int L = a.kv_lens[b];
   const int p0 = a.kv_indptr[b], p1 = a.kv_indptr[b + 1];
   const bool bad = L < 0 || L > a.max_kv_len || p0 < 0 || p1 < p0 || p1 > a.kv_indptr[a.batch] ||
                    (int64_t)(p1 - p0) * a.page_size < (int64_t)L;
-  float* outp = a.out + ((int64_t)b * H + h) * kDV + 256 * half;
+  float* outp = a.out + ((int64_t)b * H + h) * kDV + kMergeDims * chunk;
   if (bad) {
-    outp[tid] = NAN;
-    if (a.lse && half == 0 && tid == 0) a.lse[(int64_t)b * H + h] = NAN;
+    if (tid < kMergeDims) outp[tid] = NAN;
+    if (a.lse && chunk == 0 && tid == 0) a.lse[(int64_t)b * H + h] = NAN;
     return;
   }
   const int64_t slot0 = (int64_t)b * S * HG + hg;
   const int64_t sstride = (int64_t)HG * 16 * kDV;
-  const float* po = a.part_o + slot0 * (16 * kDV) + hh * kDV + 256 * half + 4 * lane;
+  const float* po = a.part_o + slot0 * (16 * kDV) + hh * kDV + kMergeDims * chunk + 4 * li;
   // first batch of partials (a split whose weight turns out 0 may hold stale data: it is
   // selected away below, never multiplied)
   f32x4 v[kMergeUnroll];
 #pragma unroll
   for (int u = 0; u < kMergeUnroll; ++u) {
-    const int s = w + 4 * u;
+    const int s = grp + kMergeGroups * u;
     v[u] = s < S ? *reinterpret_cast<const f32x4*>(po + s * sstride) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   // M = max_s m_s
@@ -692,27 +699,31 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(DecodeArgs a) 
   __syncthreads();
   tot = (sx[1][0] + sx[1][1]) + (sx[1][2] + sx[1][3]);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < S; s0 += 4 * kMergeUnroll) {
+  for (int s0 = 0; s0 < S; s0 += kMergeGroups * kMergeUnroll) {
     if (s0 > 0) {
 #pragma unroll
       for (int u = 0; u < kMergeUnroll; ++u) {
-        const int s = s0 + w + 4 * u;
+        const int s = s0 + grp + kMergeGroups * u;
         v[u] = s < S ? *reinterpret_cast<const f32x4*>(po + s * sstride) : f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
 #pragma unroll
     for (int u = 0; u < kMergeUnroll; ++u) {
-      const int s = s0 + w + 4 * u;
+      const int s = s0 + grp + kMergeGroups * u;
       const float ws = s < S ? sw[s] : 0.0f;
       if (ws != 0.0f) acc += ws * v[u];
     }
   }
-  *reinterpret_cast<f32x4*>(&sred[w][4 * lane]) = acc;
+  *reinterpret_cast<f32x4*>(&sred[grp][4 * li]) = acc;
   __syncthreads();
-  const float o = (sred[0][tid] + sred[1][tid]) + (sred[2][tid] + sred[3][tid]);
-  const float f = tot > 0.0f ? a.out_scale / tot : (tot != tot ? tot : 0.0f);
-  outp[tid] = o * f;
-  if (a.lse && half == 0 && tid == 0)
+  if (tid < kMergeDims) {
+    float o = 0.0f;
+#pragma unroll
+    for (int g = 0; g < kMergeGroups; ++g) o += sred[g][tid];
+    const float f = tot > 0.0f ? a.out_scale / tot : (tot != tot ? tot : 0.0f);
+    outp[tid] = o * f;
+  }
+  if (a.lse && chunk == 0 && tid == 0)
     a.lse[(int64_t)b * H + h] = tot > 0.0f ? (M + __log2f(tot)) * kLn2 : (tot != tot ? tot : -INFINITY);
 }
 
@@ -734,8 +745,11 @@ static hipError_t launch_fmt(const DecodeArgs& a, hipStream_t stream, const Prof
   hipError_t e = launch(mla_decode_kernel<FMT, false, TILEPAGE, NS>, grid, block, stream, ev.split_start,
                         ev.split_end, a);
   if (e != hipSuccess) return e;
-  return launch(mla_merge_kernel, dim3(2, a.num_heads, a.batch), dim3(kMergeThreads), stream, ev.merge_start,
-                ev.merge_end, a);
+  if (a.batch * a.num_heads <= 256)
+    return launch(mla_merge_kernel<64>, dim3(kDV / 64, a.num_heads, a.batch), dim3(kMergeThreads), stream,
+                  ev.merge_start, ev.merge_end, a);
+  return launch(mla_merge_kernel<256>, dim3(kDV / 256, a.num_heads, a.batch), dim3(kMergeThreads), stream,
+                ev.merge_start, ev.merge_end, a);
 }
 
 // Pages of at least a tile hold whole tiles (one descriptor per tile); shorter pages are
