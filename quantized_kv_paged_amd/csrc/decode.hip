@@ -485,22 +485,27 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
     float* const xp = sX + (buf * kWaves + (w ^ kStreams)) * (kSwapW / 4);
 #pragma unroll
     for (int tb = 0; tb < kBlocks; ++tb) *reinterpret_cast<f32x4*>(xw + 256 * tb + 4 * lane) = sp[tb];
-    __syncthreads();
-    f32x4 sq[kBlocks];
-#pragma unroll
-    for (int tb = 0; tb < kBlocks; ++tb) sq[tb] = *reinterpret_cast<const f32x4*>(xp + 256 * tb + 4 * lane);
-    // value operands of the first dim blocks, issued before the softmax arithmetic so that
-    // their latency overlaps it.  Dim block nt of token block tb is at vrb ^ 32(nt & 7), plus
+    // value operands of the first kVAhead dim blocks: they depend only on this wave's own
+    // value tile, so they are read before the swap barrier and their latency overlaps the
+    // wait for the partner.  Dim block nt of token block tb is at vrb ^ 32(nt & 7), plus
     // 256(nt >> 3) + 16 kVRow tb; the operand of the 32-token product is the pair of reads.
-    constexpr int kVAhead = 3;
+    // The base is made opaque per tile so that the 8 XORed addresses are recomputed (8 VALU)
+    // instead of being held in registers across the loop.
+    constexpr int kVAhead = 6;
+    int vrb_t = vrb;
+    asm volatile("" : "+v"(vrb_t));
     auto vread = [&](int nt) __attribute__((always_inline)) {
-      const char* p = vt + (vrb ^ (32 * (nt & 7))) + 256 * (nt >> 3);
+      const char* p = vt + (vrb_t ^ (32 * (nt & 7))) + 256 * (nt >> 3);
       const i16x4 lo = lds_read_tr16(p), hi = lds_read_tr16(p + 16 * kVRow);
       return i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     };
     i16x8 vop[16];
 #pragma unroll
     for (int nt = 0; nt < kVAhead; ++nt) vop[nt] = vread(nt);
+    __syncthreads();
+    f32x4 sq[kBlocks];
+#pragma unroll
+    for (int tb = 0; tb < kBlocks; ++tb) sq[tb] = *reinterpret_cast<const f32x4*>(xp + 256 * tb + 4 * lane);
 
     // online softmax of this stream (both waves of the pair compute the same values:
     // sp + sq and sq + sp round identically)
@@ -541,12 +546,19 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
       else pop[j] = (_Float16)pe;
     }
     l_run += rows_sum(rsum);
-    // O += P V: 16 dims per product, K = this group's 32 tokens; each operand is read kVAhead
-    // products ahead of its use
+    // O += P V: 16 dims per product, K = this group's 32 tokens.  The operands are read in
+    // batches of kVAhead dim blocks, each batch issued before the products of the previous
+    // one (scheduling barriers keep the compiler from shortening that distance, so a product
+    // does not wait on a read issued just before it)
 #pragma unroll
-    for (int nt = 0; nt < 16; ++nt) {
-      if (nt + kVAhead < 16) vop[nt + kVAhead] = vread(nt + kVAhead);
-      o[nt] = mfma16x16x32(pop, __builtin_bit_cast(Op, vop[nt]), o[nt]);
+    for (int nb = kVAhead; nb < 16 + kVAhead; nb += kVAhead) {
+#pragma unroll
+      for (int nt = nb; nt < nb + kVAhead && nt < 16; ++nt) vop[nt] = vread(nt);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int nt = nb - kVAhead; nt < nb && nt < 16; ++nt)
+        o[nt] = mfma16x16x32(pop, __builtin_bit_cast(Op, vop[nt]), o[nt]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
