@@ -181,7 +181,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=300,
+                    help="untimed steps first (clocks and memory settle over the first tens of ms)")
     ap.add_argument("--workload", default="fp8_32k", choices=["fp8_32k", "nvfp4_32k", "nvfp4_160k", "nvfp4_1m"])
     ap.add_argument("--layers", type=int, default=0, help="pool copies cycled through (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -466,6 +466,10 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
 #undef MLAQ_QK_STEP
     // the raw tile is converted: its registers take the loads of the tile kBufs ahead, which
     // are in flight during this tile's softmax and PV and the next tiles
+    // wave priority: the conversion and QK stretch runs at the highest priority, so that
+    // the other wave of the SIMD (of another workgroup) fills its gaps only while this one
+    // waits; the score swap runs at 1, the softmax and PV (latency-bound) at 0
+    __builtin_amdgcn_s_setprio(1);
     if (more) fetch(cur, st, t0 + kBufs * kTile);
     // lane: head l16, tokens 32tg + 16tb + 4grp + i
     f32x4 sp[kBlocks];
@@ -503,6 +507,7 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
 #pragma unroll
     for (int nt = 0; nt < kVAhead; ++nt) vop[nt] = vread(nt);
     __syncthreads();
+    __builtin_amdgcn_s_setprio(0);
     f32x4 sq[kBlocks];
 #pragma unroll
     for (int tb = 0; tb < kBlocks; ++tb) sq[tb] = *reinterpret_cast<const f32x4*>(xp + 256 * tb + 4 * lane);
@@ -560,8 +565,10 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
         o[nt] = mfma16x16x32(pop, __builtin_bit_cast(Op, vop[nt]), o[nt]);
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(3);   // the next tile's conversion and QK
   };
 
+  __builtin_amdgcn_s_setprio(3);
   // ---- tile loop: kBufs raw buffers per wave, each refilled (with the tile kBufs ahead) as
   //      soon as its tile is converted.  The score swap buffers alternate with the tiles.
   if constexpr (kBufs == 1) {
