@@ -309,6 +309,31 @@ def main():
                                 "bytes_moved_per_step": w.pool_tokens * (FP8_ROW + BF16_ROW) + w.batch * w.kv_len * BF16_ROW,
                                 "speedup_of_fp8_path": round(cms / ms, 2)}
         del bf
+        # the pages' intermediate fix: gather and cast only the active rows to a dense BF16
+        # workspace, then a 16-bit decode over it (identity page table into the workspace)
+        P = w.page_size
+        tok = np.arange(w.kv_len, dtype=np.int64)
+        rows_h = np.concatenate([pt.kv_indices[pt.kv_indptr[b] + tok // P].astype(np.int64) * P + tok % P
+                                 for b in range(w.batch)])
+        rows = torch.from_numpy(rows_h).cuda()
+        n_act = rows_h.shape[0]
+        gbf = torch.empty((n_act, 576), dtype=torch.bfloat16, device="cuda")
+        gind = torch.arange(n_act // P, dtype=torch.int32, device="cuda")
+        gptr = torch.arange(w.batch + 1, dtype=torch.int32, device="cuda") * (w.kv_len // P)
+        gp = qk.decode_params(w.batch, w.heads, P, w.kv_len, n_act, w.sm_scale)
+        gpp = ctypes.byref(gp)
+        gcommon = (gptr.data_ptr(), gind.data_ptr(), d["lens"].data_ptr(), out.data_ptr(), lse.data_ptr(),
+                   ws.data_ptr(), ws.numel(), stream)
+
+        def gstep(l):
+            check(L.kv_dequantize(qk.MLAQ_FP8_E4M3, fp8p[l], None, 1.0, rows.data_ptr(), n_act, w.pool_tokens,
+                                  qk.MLAQ_BF16, gbf.data_ptr(), stream))
+            check(L.mla_decode_bf16(gpp, qp, gbf.data_ptr(), *gcommon))
+        gms, _, _, _ = timed_steps(gstep, n_layers, max(20, args.steps // 4), 20, hip, torch, profile=False)
+        res["gather_cast_baseline"] = {"ms_per_step": round(gms, 5), "steps_per_s": round(1000 / gms, 1),
+                                       "bytes_moved_per_step": n_act * (FP8_ROW + 8 + 2 * BF16_ROW),
+                                       "speedup_of_fp8_path": round(gms / ms, 2)}
+        del gbf, rows
 
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, pt, host, nvfp4=(fmt == "nvfp4"))
