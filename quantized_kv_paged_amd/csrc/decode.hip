@@ -660,15 +660,18 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
 // natural-log lse.  The 256 threads are 1024 / DIMS groups of DIMS / 4 lanes; group k sums the
 // splits s = k (mod groups), each lane 4 dims, so every load of a group is DIMS x 4 contiguous
 // bytes.  Narrow chunks (DIMS = 64) spread small batches over many workgroups; wide ones
-// (DIMS = 256) keep large batches from repeating the weight computation.  The partial loads
-// of the first splits are issued before the weights are computed, so their latency overlaps
-// that of the (m, l) loads and the reductions.
+// (DIMS = 256) keep large batches from repeating the weight computation.  Every load that
+// does not depend on another one (the first batch of partials, all (m, l) pairs, the request's
+// bounds) is issued up front, so the kernel pays one memory latency before its reductions;
+// later batches of partials are loaded one batch ahead of their use.
 constexpr int kMergeThreads = 256;
 constexpr int kMergeUnroll = 4;                                  // splits per group per batch of loads
+constexpr int kMergeMLPer = (MLAQ_MAX_SPLITS + kMergeThreads - 1) / kMergeThreads;   // (m, l) per thread
 template <int DIMS>
 __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(DecodeArgs a) {
   constexpr int kMergeDims = DIMS;                                 // dims per workgroup
   constexpr int kMergeGroups = kMergeThreads / (kMergeDims / 4);   // split-strided lane groups
+  constexpr int kBatch = kMergeGroups * kMergeUnroll;              // splits per batch of loads
   __shared__ float sw[MLAQ_MAX_SPLITS];
   __shared__ __attribute__((aligned(16))) float sred[kMergeGroups][kMergeDims];
   __shared__ float sx[2][4];
@@ -676,6 +679,25 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(DecodeArgs a) 
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int grp = tid / (kMergeDims / 4), li = tid % (kMergeDims / 4);
   const int H = a.num_heads, hg = h >> 4, hh = h & 15, S = a.num_splits, HG = H / 16;
+  const int64_t slot0 = (int64_t)b * S * HG + hg;
+  const int64_t sstride = (int64_t)HG * 16 * kDV;
+  const float* po = a.part_o + slot0 * (16 * kDV) + hh * kDV + kMergeDims * chunk + 4 * li;
+  // first batch of partials (a split whose weight turns out 0 may hold stale data: it is
+  // selected away below, never multiplied), then every (m, l) of the request's splits
+  f32x4 v[kMergeUnroll];
+#pragma unroll
+  for (int u = 0; u < kMergeUnroll; ++u) {
+    const int s = grp + kMergeGroups * u;
+    v[u] = s < S ? *reinterpret_cast<const f32x4*>(po + s * sstride) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  float mv[kMergeMLPer], lv[kMergeMLPer];
+#pragma unroll
+  for (int j = 0; j < kMergeMLPer; ++j) {
+    const int s = tid + kMergeThreads * j;
+    const float* ml = a.part_ml + (slot0 + (int64_t)s * HG) * 32;
+    mv[j] = s < S ? ml[hh] : -INFINITY;
+    lv[j] = s < S ? ml[16 + hh] : 0.0f;
+  }
   const int L = a.kv_lens[b];
   const int p0 = a.kv_indptr[b], p1 = a.kv_indptr[b + 1];
   const bool bad = L < 0 || L > a.max_kv_len || p0 < 0 || p1 < p0 || p1 > a.kv_indptr[a.batch] ||
@@ -686,31 +708,21 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(DecodeArgs a) 
     if (a.lse && chunk == 0 && tid == 0) a.lse[(int64_t)b * H + h] = NAN;
     return;
   }
-  const int64_t slot0 = (int64_t)b * S * HG + hg;
-  const int64_t sstride = (int64_t)HG * 16 * kDV;
-  const float* po = a.part_o + slot0 * (16 * kDV) + hh * kDV + kMergeDims * chunk + 4 * li;
-  // first batch of partials (a split whose weight turns out 0 may hold stale data: it is
-  // selected away below, never multiplied)
-  f32x4 v[kMergeUnroll];
-#pragma unroll
-  for (int u = 0; u < kMergeUnroll; ++u) {
-    const int s = grp + kMergeGroups * u;
-    v[u] = s < S ? *reinterpret_cast<const f32x4*>(po + s * sstride) : f32x4{0.f, 0.f, 0.f, 0.f};
-  }
   // M = max_s m_s
-  float mx = -INFINITY;
-  for (int s = tid; s < S; s += kMergeThreads) mx = fmaxf(mx, a.part_ml[(slot0 + (int64_t)s * HG) * 32 + hh]);
+  float mx = mv[0];
+#pragma unroll
+  for (int j = 1; j < kMergeMLPer; ++j) mx = fmaxf(mx, mv[j]);
   mx = wave_max(mx);
   if (lane == 0) sx[0][w] = mx;
   __syncthreads();
   const float M = fmaxf(fmaxf(sx[0][0], sx[0][1]), fmaxf(sx[0][2], sx[0][3]));
   float tot = 0.0f;
-  for (int s = tid; s < S; s += kMergeThreads) {
-    const float* ml = a.part_ml + (slot0 + (int64_t)s * HG) * 32;
-    const float ms = ml[hh];
-    const float ws = ms == -INFINITY ? 0.0f : exp2f(ms - M);
-    sw[s] = ws;
-    tot += ws * ml[16 + hh];
+#pragma unroll
+  for (int j = 0; j < kMergeMLPer; ++j) {
+    const int s = tid + kMergeThreads * j;
+    const float ws = mv[j] == -INFINITY ? 0.0f : exp2f(mv[j] - M);
+    if (s < S) sw[s] = ws;
+    tot += ws * lv[j];
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
@@ -718,12 +730,13 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(DecodeArgs a) 
   __syncthreads();
   tot = (sx[1][0] + sx[1][1]) + (sx[1][2] + sx[1][3]);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < S; s0 += kMergeGroups * kMergeUnroll) {
-    if (s0 > 0) {
+  for (int s0 = 0; s0 < S; s0 += kBatch) {
+    f32x4 vn[kMergeUnroll];
+    if (s0 + kBatch < S) {
 #pragma unroll
       for (int u = 0; u < kMergeUnroll; ++u) {
-        const int s = s0 + grp + kMergeGroups * u;
-        v[u] = s < S ? *reinterpret_cast<const f32x4*>(po + s * sstride) : f32x4{0.f, 0.f, 0.f, 0.f};
+        const int s = s0 + kBatch + grp + kMergeGroups * u;
+        vn[u] = s < S ? *reinterpret_cast<const f32x4*>(po + s * sstride) : f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
 #pragma unroll
@@ -732,6 +745,8 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(DecodeArgs a) 
       const float ws = s < S ? sw[s] : 0.0f;
       if (ws != 0.0f) acc += ws * v[u];
     }
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) v[u] = vn[u];
   }
   *reinterpret_cast<f32x4*>(&sred[grp][4 * li]) = acc;
   __syncthreads();
