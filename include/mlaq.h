@@ -109,6 +109,27 @@ mlaq_status mla_decode_nvfp4(const mlaq_decode_params* p, const uint16_t* q, con
                              const int32_t* kv_indices, const int32_t* kv_lens, float* out, float* lse,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Fused append-then-attend over an NVFP4 pool (one decode call per layer and step): token
+ * kv_lens[b] - 1 of every request is the new token.  Its pool row (found through the page
+ * table like any other token) is overwritten with the NVFP4 encoding of new_kv[b], exactly as
+ * kv_quantize_nvfp4 would write it (NVFP4 article on aitop.news, implementation item 1:
+ * quantize-on-write), and the decode then attends all kv_lens[b] tokens, the new one included
+ * (implementation item 3: decode reads the packed format).  The split kernel writes the row
+ * and attends tokens 0 .. kv_lens[b] - 2; the merge pass adds the new token from the row it
+ * wrote, so one call replaces a quantize launch plus a decode.
+ * new_kv: [batch, 576] e4m3fn bytes (x = e4m3 * src_scale) or bf16 bits (new_kv_format
+ * MLAQ_FP8_E4M3 or MLAQ_BF16), 16-B aligned; the other arguments are those of
+ * mla_decode_nvfp4, with kv_data / kv_scales written.  kv_lens[b] must be >= 1 (0 gives NaN);
+ * a request whose new row lies outside the pool gets NaN and writes nothing.  The new rows
+ * must not be read by another request of the same call.  The workspace size is
+ * mlaq_decode_nvfp4_append_workspace_bytes(p): the merge pass always runs. */
+size_t mlaq_decode_nvfp4_append_workspace_bytes(const mlaq_decode_params* p);    /* (host) SIZE_MAX if p is invalid */
+mlaq_status mla_decode_nvfp4_append(const mlaq_decode_params* p, const uint16_t* q, const void* new_kv,
+                                    mlaq_format new_kv_format, float src_scale, uint8_t* kv_data,
+                                    uint8_t* kv_scales, float global_scale, const int32_t* kv_indptr,
+                                    const int32_t* kv_indices, const int32_t* kv_lens, float* out, float* lse,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Decode over a BF16 pool (the comparison path that first casts an FP8 pool to BF16,
  * as the pages' server did, and a cross-check of the quantized paths). */
 mlaq_status mla_decode_bf16(const mlaq_decode_params* p, const uint16_t* q, const uint16_t* kv,

@@ -22,7 +22,7 @@ STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_ALIGN", 4: "ERR_UNSUPP
           6: "ERR_LAUNCH", 7: "ERR_VALUE"}
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m quantized_kv_paged_amd.build` "
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python quantized_kv_paged_amd/build.py` "
                       "(or __graft_entry__.build()); there is no fallback implementation")
 
 
@@ -41,6 +41,9 @@ _SIGS = {
     "mla_decode_fp8": ([_pp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "mla_decode_nvfp4": ([_pp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "mla_decode_bf16": ([_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "mlaq_decode_nvfp4_append_workspace_bytes": ([_pp], _sz),
+    "mla_decode_nvfp4_append": ([_pp, _vp, _vp, ctypes.c_int, _f32, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _sz, _vp], ctypes.c_int),
     "kv_quantize_nvfp4": ([_vp, ctypes.c_int, _f32, _i64, _vp, _vp, _vp, _i64, _f32, _vp], ctypes.c_int),
     "kv_dequantize": ([ctypes.c_int, _vp, _vp, _f32, _vp, _i64, _i64, ctypes.c_int, _vp, _vp], ctypes.c_int),
     "mlaq_set_profile_events": ([_vp, _vp, _vp, _vp], ctypes.c_int),
@@ -148,6 +151,25 @@ def mla_decode_nvfp4(q, kv_data, kv_scales, global_scale, kv_indptr, kv_indices,
     return out, lse
 
 
+def mla_decode_nvfp4_append(q, new_kv, new_kv_format, src_scale, kv_data, kv_scales, global_scale, kv_indptr,
+                            kv_indices, kv_lens, page_size, max_kv_len, sm_scale, *, num_splits=0, out=None,
+                            lse=None, want_lse=True, workspace=None, stream=None):
+    """Fused append-then-attend: quantizes new_kv [B, 576] (e4m3fn bytes or bf16) into the pool row of
+    token kv_lens[b] - 1 of each request and decodes over all kv_lens[b] tokens; returns (out, lse)."""
+    p = _params_for(q, page_size, max_kv_len, kv_data.shape[0], sm_scale, num_splits)
+    out, lse = _decode_outputs(q, out, lse, want_lse)
+    if workspace is None:
+        n = _lib.mlaq_decode_nvfp4_append_workspace_bytes(ctypes.byref(p))
+        if n == ctypes.c_size_t(-1).value:
+            raise MlaqError(2, last_error())
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+    _check(_lib.mla_decode_nvfp4_append(ctypes.byref(p), _ptr(q), _ptr(new_kv), new_kv_format, src_scale,
+                                        _ptr(kv_data), _ptr(kv_scales), global_scale, _ptr(kv_indptr),
+                                        _ptr(kv_indices), _ptr(kv_lens), _ptr(out), _ptr(lse), _ptr(workspace),
+                                        0 if workspace is None else workspace.numel(), _stream(stream)))
+    return out, lse
+
+
 def mla_decode_bf16(q, kv, kv_indptr, kv_indices, kv_lens, page_size, max_kv_len, sm_scale, *,
                     num_splits=0, out=None, lse=None, want_lse=True, workspace=None, stream=None):
     """q: bf16 [B, H, 576]; kv: bf16 [pool, 576]; returns (out, lse)."""
@@ -181,6 +203,6 @@ def kv_dequantize(src_format, kv_data, kv_scales, scale, dst_format, *, rows=Non
     return dst
 
 
-__all__ = ["mla_decode_fp8", "mla_decode_nvfp4", "mla_decode_bf16", "kv_quantize_nvfp4", "kv_dequantize",
+__all__ = ["mla_decode_fp8", "mla_decode_nvfp4", "mla_decode_nvfp4_append", "mla_decode_bf16", "kv_quantize_nvfp4", "kv_dequantize",
            "mlaq_decode_num_splits", "mlaq_decode_workspace_bytes", "decode_params", "alloc_workspace",
            "MlaqError", "version", "last_error", "EXPORTS", "LIB_PATH"]

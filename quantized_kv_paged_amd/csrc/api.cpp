@@ -80,8 +80,18 @@ int kv_format_of(mlaq_format f) {
   return f == MLAQ_FP8_E4M3 ? mlaq::FMT_FP8 : f == MLAQ_NVFP4 ? mlaq::FMT_NVFP4 : f == MLAQ_BF16 ? mlaq::FMT_BF16 : -1;
 }
 
-size_t workspace_for(const mlaq_decode_params* p, int splits) {
-  if (splits <= 1) return 0;
+// Fused append (NVFP4): the new rows and where they go.
+struct AppendArgs {
+  const void* src = nullptr;   // [B, 576] FP8 or bf16, or null: plain decode
+  bool bf16 = false;
+  float src_scale = 1.0f;
+  uint8_t* data = nullptr;
+  uint8_t* scales = nullptr;
+};
+
+// A single split writes the output directly, unless a fused append needs the merge pass.
+size_t workspace_for(const mlaq_decode_params* p, int splits, bool append = false) {
+  if (splits <= 1 && !append) return 0;
   const size_t slots = (size_t)p->batch * (size_t)splits * (size_t)(p->num_heads / 16);
   const size_t bytes = slots * (16 * 512 * sizeof(float)) + slots * 32 * sizeof(float);
   return (bytes + 255) & ~(size_t)255;
@@ -90,7 +100,8 @@ size_t workspace_for(const mlaq_decode_params* p, int splits) {
 mlaq_status decode_common(int fmt, const mlaq_decode_params* p, const uint16_t* q, const void* kv,
                           const uint8_t* kv_scales, float scale, const int32_t* kv_indptr,
                           const int32_t* kv_indices, const int32_t* kv_lens, float* out, float* lse,
-                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                          void* workspace, size_t workspace_bytes, hipStream_t stream,
+                          const AppendArgs& app = AppendArgs()) {
   mlaq_status st = check_params(p);
   if (st != MLAQ_OK) return st;
   if (p->batch == 0) return MLAQ_OK;
@@ -106,7 +117,7 @@ mlaq_status decode_common(int fmt, const mlaq_decode_params* p, const uint16_t* 
   if (fmt != mlaq::FMT_BF16 && !finite_pos(scale))
     return fail(MLAQ_ERR_VALUE, "the KV scale must be finite and > 0 (got %g)", (double)scale);
   const int splits = resolve_splits(fmt, p);
-  const size_t need = workspace_for(p, splits);
+  const size_t need = workspace_for(p, splits, app.src != nullptr);
   if (need > 0) {
     if (!workspace) return fail(MLAQ_ERR_NULL, "workspace is NULL but %zu bytes are needed", need);
     if (workspace_bytes < need)
@@ -140,6 +151,11 @@ mlaq_status decode_common(int fmt, const mlaq_decode_params* p, const uint16_t* 
   const float s = fmt == mlaq::FMT_BF16 ? 1.0f : scale;
   a.score_scale = p->sm_scale * s * 1.4426950408889634f;
   a.out_scale = s;
+  a.app_src = app.src;
+  a.app_data = app.data;
+  a.app_scales = app.scales;
+  a.app_src_scale = app.src_scale;
+  a.app_bf16 = app.bf16 ? 1 : 0;
   const mlaq::ProfileEvents ev = g_events;
   g_events = mlaq::ProfileEvents();
   hipError_t e = mlaq::launch_decode(fmt, a, stream, ev);
@@ -191,6 +207,35 @@ mlaq_status mla_decode_nvfp4(const mlaq_decode_params* p, const uint16_t* q, con
                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return decode_common(mlaq::FMT_NVFP4, p, q, kv_data, kv_scales, global_scale, kv_indptr, kv_indices, kv_lens,
                        out, lse, workspace, workspace_bytes, stream);
+}
+
+size_t mlaq_decode_nvfp4_append_workspace_bytes(const mlaq_decode_params* p) {
+  if (check_params(p) != MLAQ_OK) return SIZE_MAX;
+  return workspace_for(p, resolve_splits(mlaq::FMT_NVFP4, p), true);
+}
+
+mlaq_status mla_decode_nvfp4_append(const mlaq_decode_params* p, const uint16_t* q, const void* new_kv,
+                                    mlaq_format new_kv_format, float src_scale, uint8_t* kv_data,
+                                    uint8_t* kv_scales, float global_scale, const int32_t* kv_indptr,
+                                    const int32_t* kv_indices, const int32_t* kv_lens, float* out, float* lse,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (new_kv_format != MLAQ_FP8_E4M3 && new_kv_format != MLAQ_BF16)
+    return fail(MLAQ_ERR_UNSUPPORTED, "mla_decode_nvfp4_append: new_kv format %d is not FP8_E4M3 or BF16",
+                (int)new_kv_format);
+  if (new_kv_format == MLAQ_FP8_E4M3 && !finite_pos(src_scale))
+    return fail(MLAQ_ERR_VALUE, "src_scale must be finite and > 0");
+  if (p && p->batch > 0) {
+    if (!new_kv) return fail(MLAQ_ERR_NULL, "new_kv is NULL");
+    if (!aligned(new_kv, 16)) return fail(MLAQ_ERR_ALIGN, "new_kv must be 16-byte aligned");
+  }
+  AppendArgs app;
+  app.src = new_kv;
+  app.bf16 = new_kv_format == MLAQ_BF16;
+  app.src_scale = src_scale;
+  app.data = kv_data;
+  app.scales = kv_scales;
+  return decode_common(mlaq::FMT_NVFP4, p, q, kv_data, kv_scales, global_scale, kv_indptr, kv_indices, kv_lens,
+                       out, lse, workspace, workspace_bytes, stream, app);
 }
 
 mlaq_status mla_decode_bf16(const mlaq_decode_params* p, const uint16_t* q, const uint16_t* kv,

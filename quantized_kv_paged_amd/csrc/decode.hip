@@ -301,14 +301,34 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
   const int tg = w % kStreams, dh = w / kStreams;   // the pair partner is w ^ kStreams
   const int H = a.num_heads;
 
-  // ---- request bounds (device data, checked without faulting)
+  // ---- request bounds (device data, checked without faulting).  With a fused append the
+  //      last of the L tokens is the new row: it is quantized into its pool row here (by one
+  //      workgroup of the request) and attended by the merge kernel, so the tiles cover L - 1.
+  const bool app = FMT == FMT_NVFP4 && a.app_src != nullptr;
   const int L = a.kv_lens[b];
   const int p0 = a.kv_indptr[b], p1 = a.kv_indptr[b + 1];
   const int npages = p1 - p0;
-  const bool bad = L < 0 || L > a.max_kv_len || p0 < 0 || npages < 0 || p1 > a.kv_indptr[a.batch] ||
+  const bool bad = L < (app ? 1 : 0) || L > a.max_kv_len || p0 < 0 || npages < 0 || p1 > a.kv_indptr[a.batch] ||
                    (int64_t)npages * a.page_size < (int64_t)L;
   const int t_begin = split * a.chunk_tokens;
-  const int t_end = bad ? t_begin : min(L, t_begin + a.chunk_tokens);
+  const int t_end = bad ? t_begin : min(app ? L - 1 : L, t_begin + a.chunk_tokens);
+  if constexpr (FMT == FMT_NVFP4) {
+    if (app && split == 0 && blockIdx.z == 0 && !bad && tid < 36) {   // block tid of the new row
+      const int j = L - 1;
+      const int page = a.kv_indices[p0 + (j >> a.page_shift)];
+      const int64_t row = ((int64_t)page << a.page_shift) + (j & (a.page_size - 1));
+      if (page >= 0 && row < a.pool_tokens) {
+        float x[16];
+        load_src_block(static_cast<const uint8_t*>(a.app_src) + (int64_t)b * kD * (a.app_bf16 ? 2 : 1),
+                       a.app_bf16 != 0, a.app_src_scale, tid, x);
+        u32x2 packed;
+        uint32_t sb;
+        nvfp4_quantize_block(x, a.out_scale, packed, sb);
+        *reinterpret_cast<u32x2*>(a.app_data + row * kNvData + 8 * tid) = packed;
+        a.app_scales[row * kNvScale + tid] = (uint8_t)sb;
+      }
+    }
+  }
   const int ntiles = t_end > t_begin ? (t_end - t_begin + kTile - 1) / kTile : 0;
 
   const int hbase = hg * 16;
@@ -674,7 +694,7 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(DecodeArgs a) 
   constexpr int kBatch = kMergeGroups * kMergeUnroll;              // splits per batch of loads
   __shared__ float sw[MLAQ_MAX_SPLITS];
   __shared__ __attribute__((aligned(16))) float sred[kMergeGroups][kMergeDims];
-  __shared__ float sx[2][4];
+  __shared__ float sx[3][4];
   const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int grp = tid / (kMergeDims / 4), li = tid % (kMergeDims / 4);
@@ -698,24 +718,66 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(DecodeArgs a) 
     mv[j] = s < S ? ml[hh] : -INFINITY;
     lv[j] = s < S ? ml[16 + hh] : 0.0f;
   }
+  // fused append: the request's last token is the new row (written by the split kernel),
+  // merged here as one more partial with m = its score, l = 1, O = its value dims
+  const bool app = a.app_src != nullptr;
   const int L = a.kv_lens[b];
   const int p0 = a.kv_indptr[b], p1 = a.kv_indptr[b + 1];
-  const bool bad = L < 0 || L > a.max_kv_len || p0 < 0 || p1 < p0 || p1 > a.kv_indptr[a.batch] ||
-                   (int64_t)(p1 - p0) * a.page_size < (int64_t)L;
+  bool bad = L < (app ? 1 : 0) || L > a.max_kv_len || p0 < 0 || p1 < p0 || p1 > a.kv_indptr[a.batch] ||
+             (int64_t)(p1 - p0) * a.page_size < (int64_t)L;
+  int64_t app_row = 0;
+  if (app && !bad) {
+    const int j = L - 1;
+    const int page = a.kv_indices[p0 + (j >> a.page_shift)];
+    app_row = ((int64_t)page << a.page_shift) + (j & (a.page_size - 1));
+    bad = page < 0 || app_row >= a.pool_tokens;
+  }
   float* outp = a.out + ((int64_t)b * H + h) * kDV + kMergeDims * chunk;
   if (bad) {
     if (tid < kMergeDims) outp[tid] = NAN;
     if (a.lse && chunk == 0 && tid == 0) a.lse[(int64_t)b * H + h] = NAN;
     return;
   }
-  // M = max_s m_s
+  // the new row's (log2-domain) score: thread t < 144 takes dims 4t .. 4t+3 (codes and
+  // scales exact in fp32, bf16 query exact); its value dims of this chunk for group 0
+  float s_new = 0.0f;
+  f32x4 v_new = {0.f, 0.f, 0.f, 0.f};
+  if (app) {
+    const uint8_t* rd = a.kv + app_row * kNvData;
+    const uint8_t* rs = a.kv_scales + app_row * kNvScale;
+    if (tid < 144) {
+      const uint32_t codes = *reinterpret_cast<const uint16_t*>(rd + 2 * tid);
+      const float sc = fp8x2_to_f32<false>(rs[tid >> 2])[0];
+      const f16x2 c01 = fp4x2_to_f16<0>(codes), c23 = fp4x2_to_f16<1>(codes);
+      const u32x2 qv = *reinterpret_cast<const u32x2*>(a.q + ((int64_t)b * H + h) * kD + 4 * tid);
+      s_new = u2f(qv[0] << 16) * ((float)c01[0] * sc) + u2f(qv[0] & 0xffff0000u) * ((float)c01[1] * sc) +
+              u2f(qv[1] << 16) * ((float)c23[0] * sc) + u2f(qv[1] & 0xffff0000u) * ((float)c23[1] * sc);
+    }
+    if (grp == 0) {
+      const int d = kMergeDims * chunk + 4 * li;
+      const uint32_t codes = *reinterpret_cast<const uint16_t*>(rd + d / 2);
+      const float sc = fp8x2_to_f32<false>(rs[d >> 4])[0];
+      const f16x2 c01 = fp4x2_to_f16<0>(codes), c23 = fp4x2_to_f16<1>(codes);
+      v_new = f32x4{(float)c01[0] * sc, (float)c01[1] * sc, (float)c23[0] * sc, (float)c23[1] * sc};
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s_new += __shfl_xor(s_new, off);
+    if (lane == 0) sx[2][w] = s_new;
+  }
+  // M = max_s m_s (and the new row's score)
   float mx = mv[0];
 #pragma unroll
   for (int j = 1; j < kMergeMLPer; ++j) mx = fmaxf(mx, mv[j]);
   mx = wave_max(mx);
   if (lane == 0) sx[0][w] = mx;
   __syncthreads();
-  const float M = fmaxf(fmaxf(sx[0][0], sx[0][1]), fmaxf(sx[0][2], sx[0][3]));
+  float M = fmaxf(fmaxf(sx[0][0], sx[0][1]), fmaxf(sx[0][2], sx[0][3]));
+  float w_new = 0.0f;
+  if (app) {
+    s_new = ((sx[2][0] + sx[2][1]) + (sx[2][2] + sx[2][3])) * a.score_scale;
+    M = fmaxf(M, s_new);
+    w_new = exp2f(s_new - M);
+  }
   float tot = 0.0f;
 #pragma unroll
   for (int j = 0; j < kMergeMLPer; ++j) {
@@ -728,8 +790,8 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(DecodeArgs a) 
   for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
   if (lane == 0) sx[1][w] = tot;
   __syncthreads();
-  tot = (sx[1][0] + sx[1][1]) + (sx[1][2] + sx[1][3]);
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  tot = (sx[1][0] + sx[1][1]) + (sx[1][2] + sx[1][3]) + w_new;
+  f32x4 acc = w_new * v_new;
   for (int s0 = 0; s0 < S; s0 += kBatch) {
     f32x4 vn[kMergeUnroll];
     if (s0 + kBatch < S) {
@@ -774,7 +836,7 @@ static hipError_t launch(K kernel, dim3 grid, dim3 block, hipStream_t stream, hi
 template <int FMT, bool TILEPAGE, int NS>
 static hipError_t launch_fmt(const DecodeArgs& a, hipStream_t stream, const ProfileEvents& ev) {
   const dim3 grid(a.num_splits, a.batch, a.num_heads / 16), block(Geo<NS>::kThreads);
-  if (a.num_splits == 1)
+  if (a.num_splits == 1 && !a.app_src)
     return launch(mla_decode_kernel<FMT, true, TILEPAGE, NS>, grid, block, stream, ev.split_start, ev.split_end, a);
   hipError_t e = launch(mla_decode_kernel<FMT, false, TILEPAGE, NS>, grid, block, stream, ev.split_start,
                         ev.split_end, a);

@@ -134,4 +134,62 @@ __device__ __forceinline__ uint32_t f32_to_e2m1_rne_sat(float y) {
   return c | ((f2u(y) >> 28) & 0x8u);
 }
 
+// One NVFP4 block of 16 fp32 values x with global scale g (NVFP4 article, format section;
+// quantize-on-write, implementation item 1): scale byte sb = e4m3_sat(fl32(fl32(amax / 6) / g)),
+// divisor sd = fl32(e4m3(sb) * g), codes e2m1_sat(fl32(x_i / sd)) packed low nibble first
+// (0 when sd == 0); a NaN in the block gives sb = 0x7F and zero codes.  IEEE fp32 division
+// and no contraction, so the bytes are the same in every kernel that quantizes.
+__device__ __forceinline__ void nvfp4_quantize_block(const float (&x)[16], float g, u32x2& packed, uint32_t& sb) {
+#pragma clang fp contract(off)
+  bool has_nan = false;
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    has_nan |= x[i] != x[i];
+    amax = fmaxf(amax, __builtin_fabsf(x[i]));
+  }
+  packed = u32x2{0u, 0u};
+  if (has_nan) {
+    sb = 0x7Fu;
+    return;
+  }
+  const float sf = (amax / 6.0f) / g;
+  sb = f32_to_e4m3_rne_sat(sf);
+  const float sd = fp8x2_to_f32<false>(sb)[0] * g;
+  if (sd != 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t c = f32_to_e2m1_rne_sat(x[i] / sd);
+      packed[i >> 3] |= c << (4 * (i & 7));
+    }
+  }
+}
+
+// The 16 source values of block k of a 576-value row: bf16 bits (exact widening) or e4m3fn
+// bytes times src_scale (fl32).
+__device__ __forceinline__ void load_src_block(const void* row, bool bf16, float src_scale, int k, float (&x)[16]) {
+#pragma clang fp contract(off)
+  if (bf16) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(row) + 16 * k);
+    const u32x4 v0 = p[0], v1 = p[1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = u2f(v0[e] << 16);
+      x[2 * e + 1] = u2f(v0[e] & 0xffff0000u);
+      x[8 + 2 * e] = u2f(v1[e] << 16);
+      x[8 + 2 * e + 1] = u2f(v1[e] & 0xffff0000u);
+    }
+  } else {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(row) + 16 * k);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const f32x2 lo = fp8x2_to_f32<false>(v[e]), hi = fp8x2_to_f32<true>(v[e]);
+      x[4 * e] = lo[0] * src_scale;
+      x[4 * e + 1] = lo[1] * src_scale;
+      x[4 * e + 2] = hi[0] * src_scale;
+      x[4 * e + 3] = hi[1] * src_scale;
+    }
+  }
+}
+
 }  // namespace mlaq

@@ -35,6 +35,13 @@ struct DecodeArgs {
   int32_t page_shift;         // log2(page_size) (page sizes are powers of two)
   float score_scale;          // sm_scale * (kv scale or global scale) * log2(e)
   float out_scale;            // kv scale or global scale
+  // fused append (NVFP4 only): the last token of every request is the new row app_src[b],
+  // quantized into its pool row by the split kernel and attended by the merge kernel
+  const void* app_src;        // FP8 bytes or bf16 bits [B, 576], or null (no append)
+  uint8_t* app_data;          // the pool's code and scale arrays, written
+  uint8_t* app_scales;
+  float app_src_scale;        // FP8 source multiplier
+  int32_t app_bf16;           // 1: bf16 source
 };
 
 struct ProfileEvents {

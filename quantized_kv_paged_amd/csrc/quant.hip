@@ -27,51 +27,10 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_kernel(QuantArgs a) {
   if (slot < 0 || slot >= a.pool_tokens) return;
 
   float x[16];
-  if (a.src_bf16) {
-    const u32x4* p = reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(a.src) + t * kD + 16 * k);
-    u32x4 v0 = p[0], v1 = p[1];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      x[2 * e] = u2f(v0[e] << 16);
-      x[2 * e + 1] = u2f(v0[e] & 0xffff0000u);
-      x[8 + 2 * e] = u2f(v1[e] << 16);
-      x[8 + 2 * e + 1] = u2f(v1[e] & 0xffff0000u);
-    }
-  } else {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(a.src) + t * kD + 16 * k);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      f32x2 lo = fp8x2_to_f32<false>(v[e]), hi = fp8x2_to_f32<true>(v[e]);
-      x[4 * e] = lo[0] * a.src_scale;
-      x[4 * e + 1] = lo[1] * a.src_scale;
-      x[4 * e + 2] = hi[0] * a.src_scale;
-      x[4 * e + 3] = hi[1] * a.src_scale;
-    }
-  }
-
-  bool has_nan = false;
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    has_nan |= x[i] != x[i];
-    amax = fmaxf(amax, __builtin_fabsf(x[i]));
-  }
+  load_src_block(reinterpret_cast<const uint8_t*>(a.src) + t * kD * (a.src_bf16 ? 2 : 1), a.src_bf16, a.src_scale, k, x);
+  u32x2 packed;
   uint32_t sb;
-  u32x2 packed = {0u, 0u};
-  if (has_nan) {
-    sb = 0x7Fu;
-  } else {
-    const float sf = (amax / 6.0f) / a.global_scale;
-    sb = f32_to_e4m3_rne_sat(sf);
-    const float sd = fp8x2_to_f32<false>(sb)[0] * a.global_scale;
-    if (sd != 0.0f) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        uint32_t c = f32_to_e2m1_rne_sat(x[i] / sd);
-        packed[i >> 3] |= c << (4 * (i & 7));
-      }
-    }
-  }
+  nvfp4_quantize_block(x, a.global_scale, packed, sb);
   *reinterpret_cast<u32x2*>(a.kv_data + slot * kNvData + 8 * k) = packed;
   a.kv_scales[slot * kNvScale + k] = (uint8_t)sb;
 }

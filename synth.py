@@ -20,6 +20,7 @@ regenerated independently (the oracle re-draws only the rows it needs):
   KV rows of request b -> (seed, 1, b, c) for chunk c of CHUNK rows, outlier mask (seed, 2, b, c)
   page permutation     -> (seed, 3)
   write-path source    -> (seed, 4)
+  appended decode rows -> (seed, 6)
   rows owned by no request (filler) -> (seed, 5, c)
 """
 from __future__ import annotations
@@ -181,6 +182,11 @@ def write_source_fp8(w: Workload) -> np.ndarray:
     """Write-path chunk: bf16-rounded N(0,1) tokens cast to FP8 e4m3fn bytes [write_tokens, 576]."""
     x = _rng(w.seed, 4).standard_normal((w.write_tokens, D), dtype=np.float32)
     return to_fp8_bytes(bf16_bits_to_fp32(to_bf16_bits(x)))
+
+
+def new_token_rows(seed: int, batch: int) -> np.ndarray:
+    """Source rows of the tokens appended by a decode step: N(0,1) fp32 [batch, 576]."""
+    return _rng(seed, 6).standard_normal((batch, D), dtype=np.float32)
 
 
 def build_fp8_pool(w: Workload, pt: PageTable, threads: int = 16) -> np.ndarray:

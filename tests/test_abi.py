@@ -137,3 +137,33 @@ def test_split_planning_and_workspace():
     assert qk.mlaq_decode_num_splits(_p(), qk.MLAQ_FP32) == 0          # not a decode KV format
     with pytest.raises(MlaqError):
         qk.mlaq_decode_workspace_bytes(_p(), qk.MLAQ_FP32)
+
+
+def _app(p, new_kv=FAKE, fmt=0, src_scale=1.0, data=FAKE, scales=FAKE, g=1.0, ws=FAKE, ws_bytes=1 << 30):
+    return qk._lib.mla_decode_nvfp4_append(ctypes.byref(p), FAKE, new_kv, fmt, src_scale, data, scales, g, FAKE,
+                                           FAKE, FAKE, FAKE, FAKE, ws, ws_bytes, None)
+
+
+def test_append_validation_and_workspace():
+    p = _p()
+    assert _app(p, fmt=qk.MLAQ_NVFP4) == ERR_UNSUPPORTED
+    assert _app(p, fmt=qk.MLAQ_FP32) == ERR_UNSUPPORTED
+    assert _app(p, fmt=qk.MLAQ_FP8_E4M3, src_scale=0.0) == ERR_VALUE
+    assert _app(p, new_kv=None) == ERR_NULL
+    assert _app(p, new_kv=FAKE + 8) == ERR_ALIGN
+    assert _app(p, scales=None) == ERR_NULL
+    assert _app(p, g=float("nan")) == ERR_VALUE
+    assert _app(_p(num_heads=24)) == ERR_SHAPE
+    assert _app(_p(batch=0), new_kv=None) == 0          # empty batch is a no-op
+    # the merge pass always runs: even one split needs the partial workspace
+    one = _p(max_kv_len=32)
+    assert qk.mlaq_decode_num_splits(one, qk.MLAQ_NVFP4) == 1
+    need = qk._lib.mlaq_decode_nvfp4_append_workspace_bytes(ctypes.byref(one))
+    assert need == ((2 * (16 * 512 * 4 + 32 * 4) + 255) // 256) * 256
+    assert _app(one, ws=None) == ERR_NULL
+    assert _app(one, ws_bytes=need - 1) == ERR_WORKSPACE
+    many = _p()
+    s = qk.mlaq_decode_num_splits(many, qk.MLAQ_NVFP4)
+    assert qk._lib.mlaq_decode_nvfp4_append_workspace_bytes(ctypes.byref(many)) == \
+        qk.mlaq_decode_workspace_bytes(many, qk.MLAQ_NVFP4) > 0 and s > 1
+    assert qk._lib.mlaq_decode_nvfp4_append_workspace_bytes(ctypes.byref(_p(num_heads=20))) == ctypes.c_size_t(-1).value
