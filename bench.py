@@ -211,7 +211,8 @@ def main():
     fcode = qk.MLAQ_FP8_E4M3 if fmt == "fp8" else qk.MLAQ_NVFP4
     splits = qk.mlaq_decode_num_splits(p, fcode)
     # one workspace large enough for every format run on this shape (the comparison legs)
-    need = max(qk.mlaq_decode_workspace_bytes(p, f) for f in (qk.MLAQ_FP8_E4M3, qk.MLAQ_NVFP4, qk.MLAQ_BF16))
+    need = max([qk.mlaq_decode_workspace_bytes(p, f) for f in (qk.MLAQ_FP8_E4M3, qk.MLAQ_NVFP4, qk.MLAQ_BF16)] +
+               [qk._lib.mlaq_decode_nvfp4_append_workspace_bytes(ctypes.byref(p))])
     ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
     out = torch.empty((w.batch, w.heads, 512), dtype=torch.float32, device="cuda")
     lse = torch.empty((w.batch, w.heads), dtype=torch.float32, device="cuda")
@@ -334,6 +335,29 @@ def main():
                                        "bytes_moved_per_step": n_act * (FP8_ROW + 8 + 2 * BF16_ROW),
                                        "speedup_of_fp8_path": round(gms / ms, 2)}
         del gbf, rows
+
+    if not args.no_extras and fmt == "nvfp4":
+        # one new token per request and step: the fused append-then-attend call against a
+        # quantize-on-write launch for the B new rows followed by the decode
+        P = w.page_size
+        last = w.kv_len - 1
+        rows_h = np.array([int(pt.kv_indices[pt.kv_indptr[b] + last // P]) * P + last % P for b in range(w.batch)],
+                          dtype=np.int64)
+        arows = torch.from_numpy(rows_h).cuda()
+        nsrc = torch.from_numpy(synth.to_bf16_bits(synth.new_token_rows(w.seed, w.batch)).view(np.int16)).cuda()
+
+        def fstep(l):
+            check(L.mla_decode_nvfp4_append(pp, qp, nsrc.data_ptr(), qk.MLAQ_BF16, 1.0, nvp[l][0], nvp[l][1], 1.0,
+                                            *common))
+
+        def sstep(l):
+            check(L.kv_quantize_nvfp4(nsrc.data_ptr(), qk.MLAQ_BF16, 1.0, w.batch, arows.data_ptr(), nvp[l][0],
+                                      nvp[l][1], w.pool_tokens, 1.0, stream))
+            check(L.mla_decode_nvfp4(pp, qp, nvp[l][0], nvp[l][1], 1.0, *common))
+        fms, _, _, _ = timed_steps(fstep, n_layers, args.steps, 50, hip, torch, profile=False)
+        sms, _, _, _ = timed_steps(sstep, n_layers, args.steps, 50, hip, torch, profile=False)
+        res["append_fused"] = {"ms_per_step": round(fms, 5), "separate_ms_per_step": round(sms, 5),
+                               "new_tokens_per_step": w.batch, "speedup_vs_separate": round(sms / fms, 3)}
 
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, pt, host, nvfp4=(fmt == "nvfp4"))

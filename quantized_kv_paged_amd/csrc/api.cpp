@@ -89,10 +89,11 @@ struct AppendArgs {
   uint8_t* scales = nullptr;
 };
 
-// A single split writes the output directly, unless a fused append needs the merge pass.
+// A single split writes the output directly; a fused append adds one partial slot per
+// request (its new token) and always takes the merge pass.
 size_t workspace_for(const mlaq_decode_params* p, int splits, bool append = false) {
   if (splits <= 1 && !append) return 0;
-  const size_t slots = (size_t)p->batch * (size_t)splits * (size_t)(p->num_heads / 16);
+  const size_t slots = (size_t)p->batch * (size_t)(splits + (append ? 1 : 0)) * (size_t)(p->num_heads / 16);
   const size_t bytes = slots * (16 * 512 * sizeof(float)) + slots * 32 * sizeof(float);
   return (bytes + 255) & ~(size_t)255;
 }
@@ -137,7 +138,8 @@ mlaq_status decode_common(int fmt, const mlaq_decode_params* p, const uint16_t* 
   a.kv_lens = kv_lens;
   a.out = out;
   a.lse = lse;
-  const size_t slots = (size_t)p->batch * splits * (p->num_heads / 16);
+  const int part_splits = splits + (app.src ? 1 : 0);
+  const size_t slots = (size_t)p->batch * part_splits * (p->num_heads / 16);
   a.part_o = need ? static_cast<float*>(workspace) : nullptr;
   a.part_ml = need ? static_cast<float*>(workspace) + slots * 16 * 512 : nullptr;
   a.pool_tokens = p->pool_tokens;
@@ -147,6 +149,7 @@ mlaq_status decode_common(int fmt, const mlaq_decode_params* p, const uint16_t* 
   a.page_shift = __builtin_ctz((unsigned)p->page_size);
   a.max_kv_len = p->max_kv_len;
   a.num_splits = splits;
+  a.part_splits = part_splits;
   a.chunk_tokens = (per > 0 ? per : 1) * tile;
   const float s = fmt == mlaq::FMT_BF16 ? 1.0f : scale;
   a.score_scale = p->sm_scale * s * 1.4426950408889634f;

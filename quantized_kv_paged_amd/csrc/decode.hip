@@ -284,6 +284,74 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// The new token of a fused append (NVFP4 pools): thread k < 36 quantizes block k of the
+// request's source row exactly as the quantize-on-write kernel does, the first head group
+// writes the codes and scales to the token's pool row, and every head group stores the row as
+// the request's extra partial (slot num_splits): m = the head's log2-domain score, l = 1,
+// O = the row's value dims.  Values are dequantized without the global scale, like the pool
+// rows the tiles convert (it is folded into the score and output scales).  A row outside the
+// pool gives an (m, l) of NaN, so the request's output is NaN.  Uses 3.3 KB of the LDS after
+// the workgroup's other LDS users are done.
+template <int NT>
+__device__ __forceinline__ void append_partial(const DecodeArgs& a, int b, int hg, int L, int p0, char* smem) {
+  const int tid = threadIdx.x, H = a.num_heads;
+  const int64_t slot = ((int64_t)b * a.part_splits + a.num_splits) * (H / 16) + hg;
+  const int j = L - 1;
+  const int page = a.kv_indices[p0 + (j >> a.page_shift)];
+  const int64_t row = ((int64_t)page << a.page_shift) + (j & (a.page_size - 1));
+  if (page < 0 || row >= a.pool_tokens) {   // uniform
+    if (tid < 32) a.part_ml[slot * 32 + tid] = NAN;
+    return;
+  }
+  float* xs = reinterpret_cast<float*>(smem);   // [576] the dequantized row
+  float* red = xs + kD;                         // [NT / 16][16] partial dot products
+  __syncthreads();
+  if (tid < 36) {
+    float x[16];
+    load_src_block(static_cast<const uint8_t*>(a.app_src) + (int64_t)b * kD * (a.app_bf16 ? 2 : 1),
+                   a.app_bf16 != 0, a.app_src_scale, tid, x);
+    u32x2 packed;
+    uint32_t sb;
+    nvfp4_quantize_block(x, a.out_scale, packed, sb);
+    if (hg == 0) {
+      *reinterpret_cast<u32x2*>(a.app_data + row * kNvData + 8 * tid) = packed;
+      a.app_scales[row * kNvScale + tid] = (uint8_t)sb;
+    }
+    const float sc = fp8x2_to_f32<false>(sb)[0];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f16x2 lo = fp4x2_to_f16<0>(packed[i >> 1] >> (16 * (i & 1)));
+      const f16x2 hi = fp4x2_to_f16<1>(packed[i >> 1] >> (16 * (i & 1)));
+      xs[16 * tid + 4 * i] = (float)lo[0] * sc;
+      xs[16 * tid + 4 * i + 1] = (float)lo[1] * sc;
+      xs[16 * tid + 4 * i + 2] = (float)hi[0] * sc;
+      xs[16 * tid + 4 * i + 3] = (float)hi[1] * sc;
+    }
+  }
+  __syncthreads();
+  // q . row per head: thread -> head tid % 16, dims [part * kPer, (part + 1) * kPer)
+  constexpr int kParts = NT / 16, kPer = kD / kParts;
+  static_assert(kD % kParts == 0, "dims split evenly");
+  const int h = tid & 15, part = tid >> 4;
+  const uint16_t* qr = a.q + ((int64_t)b * H + 16 * hg + h) * kD + part * kPer;
+  float dot = 0.0f;
+  for (int i = 0; i < kPer; ++i) dot += u2f((uint32_t)qr[i] << 16) * xs[part * kPer + i];
+  red[part * 16 + h] = dot;
+  __syncthreads();
+  if (tid < 16) {
+    float sdot = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kParts; ++k) sdot += red[k * 16 + tid];
+    a.part_ml[slot * 32 + tid] = sdot * a.score_scale;
+    a.part_ml[slot * 32 + 16 + tid] = 1.0f;
+  }
+  float* po = a.part_o + slot * (16 * kDV);
+  for (int k = tid; k < 16 * kDV / 4; k += NT) {
+    const int hh = k / (kDV / 4), d4 = k % (kDV / 4);
+    *reinterpret_cast<f32x4*>(po + hh * kDV + 4 * d4) = *reinterpret_cast<const f32x4*>(xs + 4 * d4);
+  }
+}
+
 template <int FMT, bool DIRECT, bool TILEPAGE, int NS>
 __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(DecodeArgs a) {
   constexpr int kStreams = Geo<NS>::kStreams, kTile = Geo<NS>::kTile, kWaves = Geo<NS>::kWaves;
@@ -302,8 +370,8 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
   const int H = a.num_heads;
 
   // ---- request bounds (device data, checked without faulting).  With a fused append the
-  //      last of the L tokens is the new row: it is quantized into its pool row here (by one
-  //      workgroup of the request) and attended by the merge kernel, so the tiles cover L - 1.
+  //      last of the L tokens is the new row: the tiles cover L - 1 tokens, and the workgroup
+  //      whose chunk holds token L - 1 adds the new row as one more partial (append_partial).
   const bool app = FMT == FMT_NVFP4 && a.app_src != nullptr;
   const int L = a.kv_lens[b];
   const int p0 = a.kv_indptr[b], p1 = a.kv_indptr[b + 1];
@@ -312,37 +380,24 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
                    (int64_t)npages * a.page_size < (int64_t)L;
   const int t_begin = split * a.chunk_tokens;
   const int t_end = bad ? t_begin : min(app ? L - 1 : L, t_begin + a.chunk_tokens);
-  if constexpr (FMT == FMT_NVFP4) {
-    if (app && split == 0 && blockIdx.z == 0 && !bad && tid < 36) {   // block tid of the new row
-      const int j = L - 1;
-      const int page = a.kv_indices[p0 + (j >> a.page_shift)];
-      const int64_t row = ((int64_t)page << a.page_shift) + (j & (a.page_size - 1));
-      if (page >= 0 && row < a.pool_tokens) {
-        float x[16];
-        load_src_block(static_cast<const uint8_t*>(a.app_src) + (int64_t)b * kD * (a.app_bf16 ? 2 : 1),
-                       a.app_bf16 != 0, a.app_src_scale, tid, x);
-        u32x2 packed;
-        uint32_t sb;
-        nvfp4_quantize_block(x, a.out_scale, packed, sb);
-        *reinterpret_cast<u32x2*>(a.app_data + row * kNvData + 8 * tid) = packed;
-        a.app_scales[row * kNvScale + tid] = (uint8_t)sb;
-      }
-    }
-  }
   const int ntiles = t_end > t_begin ? (t_end - t_begin + kTile - 1) / kTile : 0;
 
   const int hbase = hg * 16;
+  const bool app_here = app && !bad && t_begin <= L - 1 && L - 1 < t_begin + a.chunk_tokens;   // uniform
   if (ntiles == 0) {   // bad request or empty chunk
     if constexpr (DIRECT) {
       float* outb = a.out + ((int64_t)b * H + hbase) * kDV;
       for (int k = tid; k < 16 * kDV; k += kThreads) outb[k] = bad ? NAN : 0.0f;
       if (a.lse && tid < 16) a.lse[(int64_t)b * H + hbase + tid] = bad ? NAN : -INFINITY;
     } else {
-      const int64_t slot = ((int64_t)b * a.num_splits + split) * (H / 16) + hg;
+      const int64_t slot = ((int64_t)b * a.part_splits + split) * (H / 16) + hg;
       if (tid < 16) {
         a.part_ml[slot * 32 + tid] = -INFINITY;
         a.part_ml[slot * 32 + 16 + tid] = 0.0f;
       }
+    }
+    if constexpr (FMT == FMT_NVFP4) {
+      if (app_here) append_partial<kThreads>(a, b, hg, L, p0, smem);
     }
     return;
   }
@@ -663,7 +718,7 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
           a.lse[(int64_t)b * H + hbase + h] =
               Lsum > 0.0f ? (Mh[j] + __log2f(Lsum)) * kLn2 : (Lsum != Lsum ? Lsum : -INFINITY);
       } else {
-        const int64_t slot = ((int64_t)b * a.num_splits + split) * (H / 16) + hg;
+        const int64_t slot = ((int64_t)b * a.part_splits + split) * (H / 16) + hg;
         *reinterpret_cast<f32x4*>(a.part_o + slot * (16 * kDV) + h * kDV + d) = acc;
         if (half == 0 && (tid & 63) == 0) {
           a.part_ml[slot * 32 + h] = Mh[j];
@@ -672,6 +727,9 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
       }
     }
     if (half == 0) __syncthreads();                  // buffer reads done before the second half
+  }
+  if constexpr (FMT == FMT_NVFP4) {
+    if (app_here) append_partial<kThreads>(a, b, hg, L, p0, smem);
   }
 }
 
@@ -694,11 +752,11 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(DecodeArgs a) 
   constexpr int kBatch = kMergeGroups * kMergeUnroll;              // splits per batch of loads
   __shared__ float sw[MLAQ_MAX_SPLITS];
   __shared__ __attribute__((aligned(16))) float sred[kMergeGroups][kMergeDims];
-  __shared__ float sx[3][4];
+  __shared__ float sx[2][4];
   const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int grp = tid / (kMergeDims / 4), li = tid % (kMergeDims / 4);
-  const int H = a.num_heads, hg = h >> 4, hh = h & 15, S = a.num_splits, HG = H / 16;
+  const int H = a.num_heads, hg = h >> 4, hh = h & 15, S = a.part_splits, HG = H / 16;
   const int64_t slot0 = (int64_t)b * S * HG + hg;
   const int64_t sstride = (int64_t)HG * 16 * kDV;
   const float* po = a.part_o + slot0 * (16 * kDV) + hh * kDV + kMergeDims * chunk + 4 * li;
@@ -718,66 +776,25 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(DecodeArgs a) 
     mv[j] = s < S ? ml[hh] : -INFINITY;
     lv[j] = s < S ? ml[16 + hh] : 0.0f;
   }
-  // fused append: the request's last token is the new row (written by the split kernel),
-  // merged here as one more partial with m = its score, l = 1, O = its value dims
-  const bool app = a.app_src != nullptr;
+  // (a fused append's new token is the last partial slot; a request without it is invalid)
   const int L = a.kv_lens[b];
   const int p0 = a.kv_indptr[b], p1 = a.kv_indptr[b + 1];
-  bool bad = L < (app ? 1 : 0) || L > a.max_kv_len || p0 < 0 || p1 < p0 || p1 > a.kv_indptr[a.batch] ||
-             (int64_t)(p1 - p0) * a.page_size < (int64_t)L;
-  int64_t app_row = 0;
-  if (app && !bad) {
-    const int j = L - 1;
-    const int page = a.kv_indices[p0 + (j >> a.page_shift)];
-    app_row = ((int64_t)page << a.page_shift) + (j & (a.page_size - 1));
-    bad = page < 0 || app_row >= a.pool_tokens;
-  }
+  const bool bad = L < (a.app_src ? 1 : 0) || L > a.max_kv_len || p0 < 0 || p1 < p0 ||
+                   p1 > a.kv_indptr[a.batch] || (int64_t)(p1 - p0) * a.page_size < (int64_t)L;
   float* outp = a.out + ((int64_t)b * H + h) * kDV + kMergeDims * chunk;
   if (bad) {
     if (tid < kMergeDims) outp[tid] = NAN;
     if (a.lse && chunk == 0 && tid == 0) a.lse[(int64_t)b * H + h] = NAN;
     return;
   }
-  // the new row's (log2-domain) score: thread t < 144 takes dims 4t .. 4t+3 (codes and
-  // scales exact in fp32, bf16 query exact); its value dims of this chunk for group 0
-  float s_new = 0.0f;
-  f32x4 v_new = {0.f, 0.f, 0.f, 0.f};
-  if (app) {
-    const uint8_t* rd = a.kv + app_row * kNvData;
-    const uint8_t* rs = a.kv_scales + app_row * kNvScale;
-    if (tid < 144) {
-      const uint32_t codes = *reinterpret_cast<const uint16_t*>(rd + 2 * tid);
-      const float sc = fp8x2_to_f32<false>(rs[tid >> 2])[0];
-      const f16x2 c01 = fp4x2_to_f16<0>(codes), c23 = fp4x2_to_f16<1>(codes);
-      const u32x2 qv = *reinterpret_cast<const u32x2*>(a.q + ((int64_t)b * H + h) * kD + 4 * tid);
-      s_new = u2f(qv[0] << 16) * ((float)c01[0] * sc) + u2f(qv[0] & 0xffff0000u) * ((float)c01[1] * sc) +
-              u2f(qv[1] << 16) * ((float)c23[0] * sc) + u2f(qv[1] & 0xffff0000u) * ((float)c23[1] * sc);
-    }
-    if (grp == 0) {
-      const int d = kMergeDims * chunk + 4 * li;
-      const uint32_t codes = *reinterpret_cast<const uint16_t*>(rd + d / 2);
-      const float sc = fp8x2_to_f32<false>(rs[d >> 4])[0];
-      const f16x2 c01 = fp4x2_to_f16<0>(codes), c23 = fp4x2_to_f16<1>(codes);
-      v_new = f32x4{(float)c01[0] * sc, (float)c01[1] * sc, (float)c23[0] * sc, (float)c23[1] * sc};
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) s_new += __shfl_xor(s_new, off);
-    if (lane == 0) sx[2][w] = s_new;
-  }
-  // M = max_s m_s (and the new row's score)
+  // M = max_s m_s
   float mx = mv[0];
 #pragma unroll
   for (int j = 1; j < kMergeMLPer; ++j) mx = fmaxf(mx, mv[j]);
   mx = wave_max(mx);
   if (lane == 0) sx[0][w] = mx;
   __syncthreads();
-  float M = fmaxf(fmaxf(sx[0][0], sx[0][1]), fmaxf(sx[0][2], sx[0][3]));
-  float w_new = 0.0f;
-  if (app) {
-    s_new = ((sx[2][0] + sx[2][1]) + (sx[2][2] + sx[2][3])) * a.score_scale;
-    M = fmaxf(M, s_new);
-    w_new = exp2f(s_new - M);
-  }
+  const float M = fmaxf(fmaxf(sx[0][0], sx[0][1]), fmaxf(sx[0][2], sx[0][3]));
   float tot = 0.0f;
 #pragma unroll
   for (int j = 0; j < kMergeMLPer; ++j) {
@@ -790,8 +807,8 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(DecodeArgs a) 
   for (int off = 32; off >= 1; off >>= 1) tot += __shfl_xor(tot, off);
   if (lane == 0) sx[1][w] = tot;
   __syncthreads();
-  tot = (sx[1][0] + sx[1][1]) + (sx[1][2] + sx[1][3]) + w_new;
-  f32x4 acc = w_new * v_new;
+  tot = (sx[1][0] + sx[1][1]) + (sx[1][2] + sx[1][3]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < S; s0 += kBatch) {
     f32x4 vn[kMergeUnroll];
     if (s0 + kBatch < S) {

@@ -28,15 +28,16 @@ struct DecodeArgs {
   const int32_t* kv_lens;
   float* out;                 // [B, H, 512]
   float* lse;                 // [B, H] or null
-  float* part_o;              // [B, S, H/16, 16, 512]
-  float* part_ml;             // [B, S, H/16, 32]: m (16) then l (16)
+  float* part_o;              // [B, part_splits, H/16, 16, 512]
+  float* part_ml;             // [B, part_splits, H/16, 32]: m (16) then l (16)
   int64_t pool_tokens;
   int32_t batch, num_heads, page_size, max_kv_len, num_splits, chunk_tokens;
+  int32_t part_splits;        // partial slots per (request, head group): num_splits (+ 1 with a fused append)
   int32_t page_shift;         // log2(page_size) (page sizes are powers of two)
   float score_scale;          // sm_scale * (kv scale or global scale) * log2(e)
   float out_scale;            // kv scale or global scale
   // fused append (NVFP4 only): the last token of every request is the new row app_src[b],
-  // quantized into its pool row by the split kernel and attended by the merge kernel
+  // quantized into its pool row and turned into an extra partial by the split kernel
   const void* app_src;        // FP8 bytes or bf16 bits [B, 576], or null (no append)
   uint8_t* app_data;          // the pool's code and scale arrays, written
   uint8_t* app_scales;

@@ -155,15 +155,17 @@ def test_append_validation_and_workspace():
     assert _app(p, g=float("nan")) == ERR_VALUE
     assert _app(_p(num_heads=24)) == ERR_SHAPE
     assert _app(_p(batch=0), new_kv=None) == 0          # empty batch is a no-op
-    # the merge pass always runs: even one split needs the partial workspace
+    # the merge pass always runs and every request has one more partial slot (its new token):
+    # even one split needs the workspace
+    slot = 16 * 512 * 4 + 32 * 4
     one = _p(max_kv_len=32)
     assert qk.mlaq_decode_num_splits(one, qk.MLAQ_NVFP4) == 1
     need = qk._lib.mlaq_decode_nvfp4_append_workspace_bytes(ctypes.byref(one))
-    assert need == ((2 * (16 * 512 * 4 + 32 * 4) + 255) // 256) * 256
+    assert need == ((2 * 2 * slot + 255) // 256) * 256
     assert _app(one, ws=None) == ERR_NULL
     assert _app(one, ws_bytes=need - 1) == ERR_WORKSPACE
     many = _p()
     s = qk.mlaq_decode_num_splits(many, qk.MLAQ_NVFP4)
-    assert qk._lib.mlaq_decode_nvfp4_append_workspace_bytes(ctypes.byref(many)) == \
-        qk.mlaq_decode_workspace_bytes(many, qk.MLAQ_NVFP4) > 0 and s > 1
+    assert s > 1
+    assert qk._lib.mlaq_decode_nvfp4_append_workspace_bytes(ctypes.byref(many)) == ((2 * (s + 1) * slot + 255) // 256) * 256
     assert qk._lib.mlaq_decode_nvfp4_append_workspace_bytes(ctypes.byref(_p(num_heads=20))) == ctypes.c_size_t(-1).value
