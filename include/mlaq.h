@@ -130,6 +130,44 @@ mlaq_status mla_decode_nvfp4_append(const mlaq_decode_params* p, const uint16_t*
                                     const int32_t* kv_indices, const int32_t* kv_lens, float* out, float* lse,
                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Extend (chunked prefill) over an NVFP4 cache (NVFP4 article on aitop.news, implementation
+ * item 2): for each request b, the chunk's query tokens q[qo_indptr[b] .. qo_indptr[b+1]) attend
+ * the request's cached prefix (prefix_lens[b] tokens through the cache page table) followed by
+ * the chunk's own rows, causally: chunk token i sees the prefix, chunk tokens 0 .. i-1 and
+ * itself.  As on the page, the prefix is first dequantized into an FP8 workspace
+ * (e4m3 of fl32(e2m1 * e4m3 * global_scale) / chunk_scale: lossy, up to 6 significant bits
+ * round to 4), the chunk's FP8 rows are appended, attention runs over that workspace, and
+ * the chunk is then quantized into the cache at slot_mapping[t] (kv_quantize_nvfp4 with
+ * src_scale = chunk_scale; rows < 0 skipped).  Attention uses the FP8 decode kernels, one
+ * query token (all its heads) per workspace view.
+ *   q          bf16 [num_q, num_heads, 576]      chunk_kv  e4m3fn [num_q, 576], x = e4m3 * chunk_scale
+ *   qo_indptr  int32 [batch + 1]                  prefix_lens int32 [batch]
+ *   out        fp32 [num_q, num_heads, 512]       lse fp32 [num_q, num_heads] or NULL
+ * Device-resident lengths and pages are checked: a request whose prefix or chunk length is
+ * outside [0, max_*_len], whose pages do not cover its prefix or whose query range leaves
+ * [0, num_q) gets NaN; a prefix page outside the pool gives NaN for the tokens that see it.
+ * The workspace (mlaq_extend_workspace_bytes(p), 256-B aligned) holds batch regions of
+ * round_up(max_prefix_len + max_chunk_len, 64) FP8 rows, the per-token views and the
+ * decode partials; it is reused across layers. */
+typedef struct {              /* (host) */
+  int32_t batch;              /* requests, 0 .. 65535 */
+  int32_t num_heads;          /* multiple of 16, 16 .. 128 */
+  int32_t page_size;          /* cache page size: a power of two, 1 .. 1024 */
+  int64_t pool_tokens;        /* cache rows */
+  int32_t num_q;              /* chunk tokens over all requests (rows of q, chunk_kv, out), 0 .. 65535 */
+  int32_t max_prefix_len;     /* host bounds of prefix_lens[] and of the chunk lengths */
+  int32_t max_chunk_len;
+  int32_t num_splits;         /* KV chunks per query token in the attention; 0 = automatic */
+  float sm_scale;
+} mlaq_extend_params;
+size_t mlaq_extend_workspace_bytes(const mlaq_extend_params* p);   /* (host) SIZE_MAX if p is invalid */
+int32_t mlaq_extend_num_splits(const mlaq_extend_params* p);       /* (host) 0 if p is invalid */
+mlaq_status mla_extend_nvfp4(const mlaq_extend_params* p, const uint16_t* q, const int32_t* qo_indptr,
+                             const uint8_t* chunk_kv, float chunk_scale, uint8_t* kv_data, uint8_t* kv_scales,
+                             float global_scale, const int32_t* kv_indptr, const int32_t* kv_indices,
+                             const int32_t* prefix_lens, const int64_t* slot_mapping, float* out, float* lse,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Decode over a BF16 pool (the comparison path that first casts an FP8 pool to BF16,
  * as the pages' server did, and a cross-check of the quantized paths). */
 mlaq_status mla_decode_bf16(const mlaq_decode_params* p, const uint16_t* q, const uint16_t* kv,

@@ -21,6 +21,11 @@ What it computes, and from which passage of the pages:
                    dims of the same row).  "The Smoking Gun" page: the plan() call
                    (causal False) and the [495552, 1, 576] pool with 512 + 64 dims.
 
+  * extend.py    -- extend (chunked prefill) over an NVFP4 cache: the prefix
+                   dequantized into an FP8 workspace, the chunk's rows appended,
+                   attention of each chunk token over the rows it may see.  NVFP4
+                   article, implementation item 2.
+
 Every function here is plain and slow on purpose; the pins that tie it to the
 pages and to mathematics live in tests/test_oracle_*.py.
 """

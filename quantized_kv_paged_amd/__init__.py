@@ -32,9 +32,16 @@ class DecodeParams(ctypes.Structure):
                 ("sm_scale", ctypes.c_float)]
 
 
+class ExtendParams(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("pool_tokens", ctypes.c_int64), ("num_q", ctypes.c_int32), ("max_prefix_len", ctypes.c_int32),
+                ("max_chunk_len", ctypes.c_int32), ("num_splits", ctypes.c_int32), ("sm_scale", ctypes.c_float)]
+
+
 _lib = ctypes.CDLL(LIB_PATH)
 _vp, _i64, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 _pp = ctypes.POINTER(DecodeParams)
+_ep = ctypes.POINTER(ExtendParams)
 _SIGS = {
     "mlaq_decode_num_splits": ([_pp, ctypes.c_int], _i32),
     "mlaq_decode_workspace_bytes": ([_pp, ctypes.c_int], _sz),
@@ -44,6 +51,10 @@ _SIGS = {
     "mlaq_decode_nvfp4_append_workspace_bytes": ([_pp], _sz),
     "mla_decode_nvfp4_append": ([_pp, _vp, _vp, ctypes.c_int, _f32, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp,
                                  _sz, _vp], ctypes.c_int),
+    "mlaq_extend_workspace_bytes": ([_ep], _sz),
+    "mlaq_extend_num_splits": ([_ep], _i32),
+    "mla_extend_nvfp4": ([_ep, _vp, _vp, _vp, _f32, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+                         ctypes.c_int),
     "kv_quantize_nvfp4": ([_vp, ctypes.c_int, _f32, _i64, _vp, _vp, _vp, _i64, _f32, _vp], ctypes.c_int),
     "kv_dequantize": ([ctypes.c_int, _vp, _vp, _f32, _vp, _i64, _i64, ctypes.c_int, _vp, _vp], ctypes.c_int),
     "mlaq_set_profile_events": ([_vp, _vp, _vp, _vp], ctypes.c_int),
@@ -183,6 +194,38 @@ def mla_decode_bf16(q, kv, kv_indptr, kv_indices, kv_lens, page_size, max_kv_len
     return out, lse
 
 
+def extend_params(batch, num_heads, page_size, pool_tokens, num_q, max_prefix_len, max_chunk_len, sm_scale,
+                  num_splits=0) -> ExtendParams:
+    return ExtendParams(batch, num_heads, page_size, pool_tokens, num_q, max_prefix_len, max_chunk_len, num_splits,
+                        sm_scale)
+
+
+def mlaq_extend_workspace_bytes(p: ExtendParams) -> int:
+    n = _lib.mlaq_extend_workspace_bytes(ctypes.byref(p))
+    if n == ctypes.c_size_t(-1).value:
+        raise MlaqError(2, last_error())
+    return n
+
+
+def mla_extend_nvfp4(q, qo_indptr, chunk_kv, chunk_scale, kv_data, kv_scales, global_scale, kv_indptr, kv_indices,
+                     prefix_lens, slot_mapping, page_size, max_prefix_len, max_chunk_len, sm_scale, *,
+                     num_splits=0, out=None, lse=None, want_lse=True, workspace=None, stream=None):
+    """Extend (chunked prefill) over an NVFP4 cache: q bf16 [num_q, H, 576], chunk_kv uint8 e4m3fn
+    [num_q, 576], qo_indptr / prefix_lens int32, slot_mapping int64 [num_q]; the chunk is written into
+    kv_data / kv_scales after the attention.  Returns (out, lse)."""
+    B = qo_indptr.shape[0] - 1
+    p = extend_params(B, q.shape[1], page_size, kv_data.shape[0], q.shape[0], max_prefix_len, max_chunk_len,
+                      sm_scale, num_splits)
+    out, lse = _decode_outputs(q, out, lse, want_lse)
+    if workspace is None:
+        workspace = torch.empty(max(mlaq_extend_workspace_bytes(p), 256), dtype=torch.uint8, device=q.device)
+    _check(_lib.mla_extend_nvfp4(ctypes.byref(p), _ptr(q), _ptr(qo_indptr), _ptr(chunk_kv), chunk_scale,
+                                 _ptr(kv_data), _ptr(kv_scales), global_scale, _ptr(kv_indptr), _ptr(kv_indices),
+                                 _ptr(prefix_lens), _ptr(slot_mapping), _ptr(out), _ptr(lse), _ptr(workspace),
+                                 workspace.numel(), _stream(stream)))
+    return out, lse
+
+
 def kv_quantize_nvfp4(src, src_format, src_scale, slot_mapping, kv_data, kv_scales, global_scale, *, stream=None):
     """src: uint8 e4m3fn or bf16 [n, 576]; slot_mapping int64 [n]; writes kv_data / kv_scales rows in place."""
     n = src.shape[0]
@@ -203,6 +246,7 @@ def kv_dequantize(src_format, kv_data, kv_scales, scale, dst_format, *, rows=Non
     return dst
 
 
-__all__ = ["mla_decode_fp8", "mla_decode_nvfp4", "mla_decode_nvfp4_append", "mla_decode_bf16", "kv_quantize_nvfp4", "kv_dequantize",
+__all__ = ["mla_decode_fp8", "mla_decode_nvfp4", "mla_decode_nvfp4_append", "mla_decode_bf16", "mla_extend_nvfp4",
+           "extend_params", "mlaq_extend_workspace_bytes", "kv_quantize_nvfp4", "kv_dequantize",
            "mlaq_decode_num_splits", "mlaq_decode_workspace_bytes", "decode_params", "alloc_workspace",
            "MlaqError", "version", "last_error", "EXPORTS", "LIB_PATH"]

@@ -166,6 +166,51 @@ mlaq_status decode_common(int fmt, const mlaq_decode_params* p, const uint16_t* 
   return MLAQ_OK;
 }
 
+// Extend: workspace layout (FP8 regions, per-token views, decode partials), each part
+// 256-byte aligned, and the decode parameters of the per-token views.
+struct ExtendLayout {
+  int region_rows = 0, npp = 0;
+  size_t rows_off = 0, idx_off = 0, lens_off = 0, indptr_off = 0, part_off = 0, part_bytes = 0, total = 0;
+  mlaq_decode_params dp{};
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+mlaq_status extend_layout(const mlaq_extend_params* p, ExtendLayout& L) {
+  if (!p) return fail(MLAQ_ERR_NULL, "params is NULL");
+  if (p->batch < 0 || p->batch > 65535) return fail(MLAQ_ERR_SHAPE, "batch %d not in [0, 65535]", p->batch);
+  if (p->num_q < 0 || p->num_q > 65535) return fail(MLAQ_ERR_SHAPE, "num_q %d not in [0, 65535]", p->num_q);
+  if (p->max_prefix_len < 0 || p->max_chunk_len < 0 ||
+      (int64_t)p->max_prefix_len + p->max_chunk_len > MLAQ_MAX_KV_LEN)
+    return fail(MLAQ_ERR_SHAPE, "max_prefix_len %d / max_chunk_len %d out of range", p->max_prefix_len,
+                p->max_chunk_len);
+  if (p->num_q > 0 && p->max_chunk_len < 1) return fail(MLAQ_ERR_SHAPE, "num_q > 0 needs max_chunk_len >= 1");
+  const int64_t span = (int64_t)p->max_prefix_len + p->max_chunk_len;
+  L.region_rows = (int)((span + mlaq::kExtendPage - 1) / mlaq::kExtendPage * mlaq::kExtendPage);
+  L.npp = L.region_rows / mlaq::kExtendPage;
+  L.dp.batch = p->num_q;
+  L.dp.num_heads = p->num_heads;
+  L.dp.page_size = mlaq::kExtendPage;
+  L.dp.max_kv_len = (int32_t)span;
+  L.dp.pool_tokens = (int64_t)(p->batch > 0 ? p->batch : 1) * (L.region_rows > 0 ? L.region_rows : 1);
+  L.dp.num_splits = p->num_splits;
+  L.dp.sm_scale = p->sm_scale;
+  mlaq_status st = check_params(&L.dp);
+  if (st != MLAQ_OK) return st;
+  if (p->page_size < 1 || p->page_size > 1024 || (p->page_size & (p->page_size - 1)))
+    return fail(MLAQ_ERR_SHAPE, "page_size %d: must be a power of two in [1, 1024]", p->page_size);
+  if (p->pool_tokens <= 0 || p->pool_tokens > ((int64_t)1 << 40))
+    return fail(MLAQ_ERR_SHAPE, "pool_tokens %lld out of range", (long long)p->pool_tokens);
+  L.rows_off = 0;
+  L.idx_off = align256((size_t)p->batch * L.region_rows * 576);
+  L.lens_off = L.idx_off + align256((size_t)p->num_q * L.npp * 4);
+  L.indptr_off = L.lens_off + align256((size_t)p->num_q * 4);
+  L.part_off = L.indptr_off + align256((size_t)(p->num_q + 1) * 4);
+  L.part_bytes = workspace_for(&L.dp, resolve_splits(mlaq::FMT_FP8, &L.dp));
+  L.total = L.part_off + L.part_bytes;
+  return MLAQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -239,6 +284,73 @@ mlaq_status mla_decode_nvfp4_append(const mlaq_decode_params* p, const uint16_t*
   app.scales = kv_scales;
   return decode_common(mlaq::FMT_NVFP4, p, q, kv_data, kv_scales, global_scale, kv_indptr, kv_indices, kv_lens,
                        out, lse, workspace, workspace_bytes, stream, app);
+}
+
+size_t mlaq_extend_workspace_bytes(const mlaq_extend_params* p) {
+  ExtendLayout L;
+  if (extend_layout(p, L) != MLAQ_OK) return SIZE_MAX;
+  return L.total;
+}
+
+int32_t mlaq_extend_num_splits(const mlaq_extend_params* p) {
+  ExtendLayout L;
+  if (extend_layout(p, L) != MLAQ_OK) return 0;
+  return resolve_splits(mlaq::FMT_FP8, &L.dp);
+}
+
+mlaq_status mla_extend_nvfp4(const mlaq_extend_params* p, const uint16_t* q, const int32_t* qo_indptr,
+                             const uint8_t* chunk_kv, float chunk_scale, uint8_t* kv_data, uint8_t* kv_scales,
+                             float global_scale, const int32_t* kv_indptr, const int32_t* kv_indices,
+                             const int32_t* prefix_lens, const int64_t* slot_mapping, float* out, float* lse,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  ExtendLayout L;
+  mlaq_status st = extend_layout(p, L);
+  if (st != MLAQ_OK) return st;
+  if (!finite_pos(chunk_scale)) return fail(MLAQ_ERR_VALUE, "chunk_scale must be finite and > 0");
+  if (!finite_pos(global_scale)) return fail(MLAQ_ERR_VALUE, "global_scale must be finite and > 0");
+  if (p->batch == 0 || p->num_q == 0) return MLAQ_OK;
+  if (!q || !qo_indptr || !chunk_kv || !kv_data || !kv_scales || !kv_indptr || !kv_indices || !prefix_lens ||
+      !slot_mapping || !out)
+    return fail(MLAQ_ERR_NULL, "a required pointer is NULL");
+  if (!aligned(q, 16) || !aligned(chunk_kv, 16) || !aligned(kv_data, 16) || !aligned(out, 16))
+    return fail(MLAQ_ERR_ALIGN, "q, chunk_kv, kv_data and out must be 16-byte aligned");
+  if (!aligned(kv_scales, 4) || !aligned(qo_indptr, 4) || !aligned(kv_indptr, 4) || !aligned(kv_indices, 4) ||
+      !aligned(prefix_lens, 4) || (lse && !aligned(lse, 4)) || !aligned(slot_mapping, 8))
+    return fail(MLAQ_ERR_ALIGN, "kv_scales, index and length arrays need 4-byte alignment, slot_mapping 8-byte");
+  if (!workspace) return fail(MLAQ_ERR_NULL, "workspace is NULL but %zu bytes are needed", L.total);
+  if (workspace_bytes < L.total)
+    return fail(MLAQ_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, L.total);
+  if (!aligned(workspace, 256)) return fail(MLAQ_ERR_ALIGN, "workspace must be 256-byte aligned");
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  mlaq::ExtendArgs a;
+  a.qo_indptr = qo_indptr;
+  a.prefix_lens = prefix_lens;
+  a.kv_indptr = kv_indptr;
+  a.kv_indices = kv_indices;
+  a.kv_data = kv_data;
+  a.kv_scales = kv_scales;
+  a.chunk_kv = chunk_kv;
+  a.ws_rows = ws + L.rows_off;
+  a.view_indices = reinterpret_cast<int32_t*>(ws + L.idx_off);
+  a.view_lens = reinterpret_cast<int32_t*>(ws + L.lens_off);
+  a.view_indptr = reinterpret_cast<int32_t*>(ws + L.indptr_off);
+  a.pool_tokens = p->pool_tokens;
+  a.batch = p->batch;
+  a.num_q = p->num_q;
+  a.page_size = p->page_size;
+  a.page_shift = __builtin_ctz((unsigned)p->page_size);
+  a.max_prefix_len = p->max_prefix_len;
+  a.max_chunk_len = p->max_chunk_len;
+  a.region_rows = L.region_rows;
+  a.global_scale = global_scale;
+  a.chunk_scale = chunk_scale;
+  hipError_t e = mlaq::launch_extend_views(a, stream);
+  if (e != hipSuccess) return fail(MLAQ_ERR_LAUNCH, "extend view launch failed: %s", hipGetErrorString(e));
+  st = decode_common(mlaq::FMT_FP8, &L.dp, q, a.ws_rows, nullptr, chunk_scale, a.view_indptr, a.view_indices,
+                     a.view_lens, out, lse, L.part_bytes ? ws + L.part_off : nullptr, L.part_bytes, stream);
+  if (st != MLAQ_OK) return st;
+  return kv_quantize_nvfp4(chunk_kv, MLAQ_FP8_E4M3, chunk_scale, p->num_q, slot_mapping, kv_data, kv_scales,
+                           p->pool_tokens, global_scale, stream);
 }
 
 mlaq_status mla_decode_bf16(const mlaq_decode_params* p, const uint16_t* q, const uint16_t* kv,

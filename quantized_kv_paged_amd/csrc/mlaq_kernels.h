@@ -73,4 +73,24 @@ struct DequantArgs {
 };
 hipError_t launch_dequantize(const DequantArgs& a, hipStream_t stream);
 
+// Extend over an NVFP4 cache: per-request FP8 workspace regions and per-token causal views.
+constexpr int kExtendPage = 64;   // rows per page of the workspace views
+struct ExtendArgs {
+  const int32_t* qo_indptr;   // [B + 1] chunk-token offsets
+  const int32_t* prefix_lens; // [B]
+  const int32_t* kv_indptr;   // cache page table of the prefixes
+  const int32_t* kv_indices;
+  const uint8_t* kv_data;     // NVFP4 cache
+  const uint8_t* kv_scales;
+  const uint8_t* chunk_kv;    // e4m3fn [num_q, 576]
+  uint8_t* ws_rows;           // e4m3fn [B, region_rows, 576]
+  int32_t* view_indptr;       // [num_q + 1]
+  int32_t* view_indices;      // [num_q, region_rows / kExtendPage]
+  int32_t* view_lens;         // [num_q]
+  int64_t pool_tokens;
+  int32_t batch, num_q, page_size, page_shift, max_prefix_len, max_chunk_len, region_rows;
+  float global_scale, chunk_scale;
+};
+hipError_t launch_extend_views(const ExtendArgs& a, hipStream_t stream);
+
 }  // namespace mlaq

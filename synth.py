@@ -21,6 +21,7 @@ regenerated independently (the oracle re-draws only the rows it needs):
   page permutation     -> (seed, 3)
   write-path source    -> (seed, 4)
   appended decode rows -> (seed, 6)
+  extend chunk rows    -> (seed, 7)
   rows owned by no request (filler) -> (seed, 5, c)
 """
 from __future__ import annotations
@@ -187,6 +188,11 @@ def write_source_fp8(w: Workload) -> np.ndarray:
 def new_token_rows(seed: int, batch: int) -> np.ndarray:
     """Source rows of the tokens appended by a decode step: N(0,1) fp32 [batch, 576]."""
     return _rng(seed, 6).standard_normal((batch, D), dtype=np.float32)
+
+
+def extend_chunk_rows(seed: int, n: int) -> np.ndarray:
+    """KV rows of an extend chunk (n tokens over all requests): N(0,1) fp32 [n, 576]."""
+    return _rng(seed, 7).standard_normal((n, D), dtype=np.float32)
 
 
 def build_fp8_pool(w: Workload, pt: PageTable, threads: int = 16) -> np.ndarray:

@@ -1,0 +1,93 @@
+"""Extend (chunked prefill) over an NVFP4 cache, through the C ABI, against the oracle.
+
+Checked per call: the FP8 workspace rows the gather kernel builds (prefix dequantized to e4m3
+in the chunk's scale, chunk rows appended) are bit-exact; the attention of every chunk token
+over the rows it may see is within the decode tolerances; the chunk's rows are written to the
+cache bit-exactly and no other cache row changes."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from cases import assert_parity, build_case
+from oracle import attention, codecs, extend
+from oracle import nvfp4 as onv
+
+pytestmark = pytest.mark.gpu
+
+
+def _t(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _run(prefix, chunk, page_size, seed, splits=(0,), g=1.0, chunk_scale=1.0, heads=16, prefix_lens_dev=None):
+    import quantized_kv_paged_amd as qk
+    prefix, chunk = np.asarray(prefix, np.int32), np.asarray(chunk, np.int32)
+    B = len(prefix)
+    c = build_case("nvfp4", prefix + chunk, page_size, seed, heads=heads, outlier_p=0.01, g=g)
+    qo = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
+    nq = int(qo[-1])
+    q_bits = synth.q_bits(seed + 100, nq, heads)
+    ckv = synth.to_fp8_bytes(synth.extend_chunk_rows(seed, nq) / np.float32(chunk_scale))
+    slots = np.concatenate([attention.gather_rows(c.pt.kv_indptr, c.pt.kv_indices, page_size, b,
+                                                  int(prefix[b] + chunk[b]))[prefix[b]:] for b in range(B)])
+    # oracle: workspace bytes, attention, cache after the write
+    ws_ref, out_ref, lse_ref = [], np.zeros((nq, heads, 512)), np.zeros((nq, heads))
+    q64 = codecs.bf16_bits_to_f64(q_bits)
+    for b in range(B):
+        rows = attention.gather_rows(c.pt.kv_indptr, c.pt.kv_indices, page_size, b, int(prefix[b]))
+        ws = np.concatenate([extend.workspace_prefix(c.nv_data[rows], c.nv_scales[rows], c.scale, chunk_scale),
+                             ckv[qo[b]:qo[b + 1]]])
+        ws_ref.append(ws)
+        out_ref[qo[b]:qo[b + 1]], lse_ref[qo[b]:qo[b + 1]] = extend.extend_request(
+            q64[qo[b]:qo[b + 1]], ws, int(prefix[b]), chunk_scale, c.w.sm_scale)
+    new_d, new_s = onv.quantize_fp8_rows(ckv, chunk_scale, c.scale)
+    pool_d, pool_s = c.nv_data.copy(), c.nv_scales.copy()
+    pool_d[slots], pool_s[slots] = new_d, new_s
+    mp, mc = int(prefix.max()), int(chunk.max())
+    region = -(-(mp + mc) // 64) * 64
+    for s in splits:
+        data, scales = _t(c.nv_data), _t(c.nv_scales)
+        p = qk.extend_params(B, heads, page_size, data.shape[0], nq, mp, mc, c.w.sm_scale, s)
+        ws = torch.zeros(qk.mlaq_extend_workspace_bytes(p), dtype=torch.uint8, device="cuda")
+        pl = _t(prefix if prefix_lens_dev is None else prefix_lens_dev)
+        out, lse = qk.mla_extend_nvfp4(_t(q_bits.view(np.int16)).view(torch.bfloat16), _t(qo), _t(ckv), chunk_scale,
+                                       data, scales, c.scale, _t(c.pt.kv_indptr), _t(c.pt.kv_indices), pl,
+                                       _t(slots.astype(np.int64)), page_size, mp, mc, c.w.sm_scale, num_splits=s,
+                                       workspace=ws)
+        torch.cuda.synchronize()
+        out, lse = out.double().cpu().numpy(), lse.double().cpu().numpy()
+        wsh = ws.cpu().numpy()
+        if prefix_lens_dev is None:
+            for b in range(B):
+                n = int(prefix[b] + chunk[b])
+                got = wsh[b * region * 576:(b * region + n) * 576].reshape(n, 576)
+                np.testing.assert_array_equal(got, ws_ref[b], err_msg=f"workspace request {b}")
+            mx, rel = assert_parity(out, lse, out_ref, lse_ref, tag=f"extend splits={s}")
+            print(f"[extend P{page_size} g={c.scale:.4g} cs={chunk_scale}] splits={s} max-abs {mx:.2e} rel-L2 {rel:.2e}",
+                  flush=True)
+        np.testing.assert_array_equal(data.cpu().numpy(), pool_d)
+        np.testing.assert_array_equal(scales.cpu().numpy(), pool_s)
+    return out, lse, out_ref, lse_ref, qo
+
+
+def test_extend_ragged_prefixes_and_chunks():
+    """Empty prefix, prefixes and chunks across page and tile edges; one and several splits."""
+    _run([0, 100, 700], [5, 64, 33], 64, seed=51, splits=(0, 1, 3))
+
+
+@pytest.mark.parametrize("g,cs", [(None, 1.0), (0.37, 0.75)])
+def test_extend_scales(g, cs):
+    _run([129, 40], [17, 1], 16, seed=52, splits=(0, 2), g=g, chunk_scale=cs)
+
+
+def test_extend_32_heads():
+    _run([300], [20], 64, seed=53, heads=32)
+
+
+def test_extend_bad_prefix_length_gives_nan_for_its_tokens():
+    prefix, chunk = [50, 80], [4, 3]
+    bad = np.asarray([50, 10 ** 6], np.int32)                 # above max_prefix_len
+    out, lse, out_ref, lse_ref, qo = _run(prefix, chunk, 64, seed=54, prefix_lens_dev=bad)
+    assert np.isnan(out[qo[1]:qo[2]]).all() and np.isnan(lse[qo[1]:qo[2]]).all()
+    assert_parity(out[:qo[1]], lse[:qo[1]], out_ref[:qo[1]], lse_ref[:qo[1]], tag="extend good request")
