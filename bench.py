@@ -369,6 +369,39 @@ def main():
         res["append_fused"] = {"ms_per_step": round(fms, 5), "separate_ms_per_step": round(sms, 5),
                                "new_tokens_per_step": w.batch, "speedup_vs_separate": round(sms / fms, 3)}
 
+        # extend (chunked prefill) over the cache: the first 4 requests take a 256-token chunk
+        # after a prefix of the rest of their context (prefix dequantized to an FP8 workspace,
+        # per-token causal views attended by the FP8 decode kernels, chunk written back)
+        EB, EC = min(4, w.batch), 256
+        EP = w.kv_len - EC
+        nq = EB * EC
+        tok = np.arange(EP, w.kv_len, dtype=np.int64)
+        eslots = torch.from_numpy(np.concatenate(
+            [pt.kv_indices[pt.kv_indptr[b] + tok // P].astype(np.int64) * P + tok % P for b in range(EB)])).cuda()
+        eqo = torch.arange(EB + 1, dtype=torch.int32, device="cuda") * EC
+        epl = torch.full((EB,), EP, dtype=torch.int32, device="cuda")
+        eq = torch.from_numpy(synth.q_bits(w.seed + 7, nq, w.heads).view(np.int16)).cuda()
+        eckv = torch.from_numpy(synth.to_fp8_bytes(synth.extend_chunk_rows(w.seed, nq))).cuda()
+        ep = qk.extend_params(EB, w.heads, P, w.pool_tokens, nq, EP, EC, w.sm_scale)
+        ews = torch.empty(qk.mlaq_extend_workspace_bytes(ep), dtype=torch.uint8, device="cuda")
+        eout = torch.empty((nq, w.heads, 512), dtype=torch.float32, device="cuda")
+        else_ = torch.empty((nq, w.heads), dtype=torch.float32, device="cuda")
+
+        def estep(l):
+            check(L.mla_extend_nvfp4(ctypes.byref(ep), eq.data_ptr(), eqo.data_ptr(), eckv.data_ptr(), 1.0,
+                                     nvp[l][0], nvp[l][1], 1.0, d["indptr"].data_ptr(), d["indices"].data_ptr(),
+                                     epl.data_ptr(), eslots.data_ptr(), eout.data_ptr(), else_.data_ptr(),
+                                     ews.data_ptr(), ews.numel(), stream))
+        ems, esplit, emerge, _ = timed_steps(estep, n_layers, 10, 3, hip, torch)
+        eflops = EB * sum(2 * w.heads * (EP + i + 1) * (576 + 512) for i in range(EC))
+        res["extend"] = {"requests": EB, "prefix_tokens": EP, "chunk_tokens": EC, "ms_per_call": round(ems, 4),
+                         "chunk_tokens_per_s": round(nq / (ems * 1e-3), 1),
+                         "attention_kernel_ms": round(esplit + emerge, 4),
+                         "attention_tflops": round(eflops / (esplit * 1e-3) / 1e12, 1),
+                         "frac_of_fp16_mfma_peak": round(eflops / (esplit * 1e-3) / 2.5e15, 4),
+                         "workspace_rows_read_per_call_gb": round(
+                             EB * sum(EP + i + 1 for i in range(EC)) * FP8_ROW / 1e9, 2)}
+
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, pt, host, nvfp4=(fmt == "nvfp4"))
     print(json.dumps(res))

@@ -91,3 +91,9 @@ def test_extend_bad_prefix_length_gives_nan_for_its_tokens():
     out, lse, out_ref, lse_ref, qo = _run(prefix, chunk, 64, seed=54, prefix_lens_dev=bad)
     assert np.isnan(out[qo[1]:qo[2]]).all() and np.isnan(lse[qo[1]:qo[2]]).all()
     assert_parity(out[:qo[1]], lse[:qo[1]], out_ref[:qo[1]], lse_ref[:qo[1]], tag="extend good request")
+
+
+def test_initial_prefill_is_extend_with_empty_prefix():
+    """The initial-prefill path of the pages (attention over the chunk's own FP8 KV, then the NVFP4
+    write; no cache read) is extend with every prefix empty: causal attention inside each prompt."""
+    _run([0, 0, 0], [1, 70, 257], 64, seed=55, splits=(0, 2))
