@@ -1,5 +1,6 @@
 // Host side of the mlaq C ABI: argument validation, split planning, workspace layout and
 // kernel launches.  Nothing here touches device memory or synchronises.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -170,6 +171,8 @@ mlaq_status decode_common(int fmt, const mlaq_decode_params* p, const uint16_t* 
 // 256-byte aligned, and the decode parameters of the per-token views.
 struct ExtendLayout {
   int region_rows = 0, npp = 0;
+  bool tiled = false;             // 16 heads: shared-tile extend attention; otherwise decode views
+  int tsplits = 1, tiles_per_split = 1;
   size_t rows_off = 0, idx_off = 0, lens_off = 0, indptr_off = 0, part_off = 0, part_bytes = 0, total = 0;
   mlaq_decode_params dp{};
 };
@@ -206,7 +209,23 @@ mlaq_status extend_layout(const mlaq_extend_params* p, ExtendLayout& L) {
   L.lens_off = L.idx_off + align256((size_t)p->num_q * L.npp * 4);
   L.indptr_off = L.lens_off + align256((size_t)p->num_q * 4);
   L.part_off = L.indptr_off + align256((size_t)(p->num_q + 1) * 4);
-  L.part_bytes = workspace_for(&L.dp, resolve_splits(mlaq::FMT_FP8, &L.dp));
+  L.tiled = p->num_heads == 16;
+  if (L.tiled) {
+    // KV splits so that the workgroups (one per kXT chunk tokens of a request, one per CU)
+    // cover the CUs at least once; each split takes a whole number of 32-row tiles
+    const int tile = mlaq::extend_attn_tile_rows(), per_group = mlaq::extend_attn_tokens_per_group();
+    const int max_tiles = (int)((span + tile - 1) / tile);
+    const int64_t groups = (int64_t)p->batch * ((p->max_chunk_len + per_group - 1) / per_group);
+    int s_ = p->num_splits > 0 ? p->num_splits
+                               : (int)std::min<int64_t>(MLAQ_MAX_SPLITS, groups > 0 ? (mlaq::kComputeUnits + groups - 1) / groups : 1);
+    s_ = std::max(1, std::min(s_, std::max(1, max_tiles)));
+    L.tiles_per_split = std::max(1, (max_tiles + s_ - 1) / s_);
+    L.tsplits = (max_tiles + L.tiles_per_split - 1) / L.tiles_per_split;
+    if (L.tsplits < 1) L.tsplits = 1;
+    L.part_bytes = L.tsplits > 1 ? align256((size_t)p->num_q * L.tsplits * (16 * 512 * 4 + 32 * 4)) : 0;
+  } else {
+    L.part_bytes = workspace_for(&L.dp, resolve_splits(mlaq::FMT_FP8, &L.dp));
+  }
   L.total = L.part_off + L.part_bytes;
   return MLAQ_OK;
 }
@@ -295,7 +314,7 @@ size_t mlaq_extend_workspace_bytes(const mlaq_extend_params* p) {
 int32_t mlaq_extend_num_splits(const mlaq_extend_params* p) {
   ExtendLayout L;
   if (extend_layout(p, L) != MLAQ_OK) return 0;
-  return resolve_splits(mlaq::FMT_FP8, &L.dp);
+  return L.tiled ? L.tsplits : resolve_splits(mlaq::FMT_FP8, &L.dp);
 }
 
 mlaq_status mla_extend_nvfp4(const mlaq_extend_params* p, const uint16_t* q, const int32_t* qo_indptr,
@@ -344,11 +363,63 @@ mlaq_status mla_extend_nvfp4(const mlaq_extend_params* p, const uint16_t* q, con
   a.region_rows = L.region_rows;
   a.global_scale = global_scale;
   a.chunk_scale = chunk_scale;
+  a.write_pages = L.tiled ? 0 : 1;
+  a.nan_out = L.tiled && L.tsplits == 1 ? out : nullptr;
+  a.nan_lse = L.tiled && L.tsplits == 1 ? lse : nullptr;
   hipError_t e = mlaq::launch_extend_views(a, stream);
   if (e != hipSuccess) return fail(MLAQ_ERR_LAUNCH, "extend view launch failed: %s", hipGetErrorString(e));
-  st = decode_common(mlaq::FMT_FP8, &L.dp, q, a.ws_rows, nullptr, chunk_scale, a.view_indptr, a.view_indices,
-                     a.view_lens, out, lse, L.part_bytes ? ws + L.part_off : nullptr, L.part_bytes, stream);
-  if (st != MLAQ_OK) return st;
+  if (L.tiled) {
+    mlaq::ExtendAttnArgs x;
+    x.q = q;
+    x.ws_rows = a.ws_rows;
+    x.qo_indptr = qo_indptr;
+    x.prefix_lens = prefix_lens;
+    x.kv_indptr = kv_indptr;
+    x.out = out;
+    x.lse = lse;
+    x.part_o = L.part_bytes ? reinterpret_cast<float*>(ws + L.part_off) : nullptr;
+    x.part_ml = L.part_bytes ? x.part_o + (size_t)p->num_q * L.tsplits * 16 * 512 : nullptr;
+    x.batch = p->batch;
+    x.num_q = p->num_q;
+    x.page_size = p->page_size;
+    x.max_prefix_len = p->max_prefix_len;
+    x.max_chunk_len = p->max_chunk_len;
+    x.region_rows = L.region_rows;
+    x.num_splits = L.tsplits;
+    x.tiles_per_split = L.tiles_per_split;
+    x.score_scale = p->sm_scale * chunk_scale * 1.4426950408889634f;
+    x.out_scale = chunk_scale;
+    const mlaq::ProfileEvents ev = g_events;
+    g_events = mlaq::ProfileEvents();
+    if (ev.split_start) hipEventRecord(ev.split_start, stream);
+    e = mlaq::launch_extend_attn(x, stream);
+    if (ev.split_end) hipEventRecord(ev.split_end, stream);
+    if (e != hipSuccess) return fail(MLAQ_ERR_LAUNCH, "extend attention launch failed: %s", hipGetErrorString(e));
+    if (L.tsplits > 1) {
+      mlaq::DecodeArgs m{};
+      m.kv_indptr = a.view_indptr;
+      m.kv_lens = a.view_lens;
+      m.out = out;
+      m.lse = lse;
+      m.part_o = x.part_o;
+      m.part_ml = x.part_ml;
+      m.batch = p->num_q;
+      m.num_heads = 16;
+      m.page_size = mlaq::kExtendPage;
+      m.max_kv_len = L.dp.max_kv_len;
+      m.num_splits = L.tsplits;
+      m.part_splits = L.tsplits;
+      m.out_scale = chunk_scale;
+      if (ev.merge_start) hipEventRecord(ev.merge_start, stream);
+      e = mlaq::launch_merge(m, stream);
+      if (ev.merge_end) hipEventRecord(ev.merge_end, stream);
+      if (e != hipSuccess) return fail(MLAQ_ERR_LAUNCH, "extend merge launch failed: %s", hipGetErrorString(e));
+    }
+  } else {
+    st = decode_common(mlaq::FMT_FP8, &L.dp, q, a.ws_rows, nullptr, chunk_scale, a.view_indptr, a.view_indices,
+                       a.view_lens, out, lse, L.part_bytes ? ws + L.part_off : nullptr, L.part_bytes, stream);
+    if (st != MLAQ_OK) return st;
+  }
   return kv_quantize_nvfp4(chunk_kv, MLAQ_FP8_E4M3, chunk_scale, p->num_q, slot_mapping, kv_data, kv_scales,
                            p->pool_tokens, global_scale, stream);
 }

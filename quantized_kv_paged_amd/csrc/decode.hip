@@ -850,6 +850,13 @@ static hipError_t launch(K kernel, dim3 grid, dim3 block, hipStream_t stream, hi
   return hipGetLastError();
 }
 
+static hipError_t launch_fmt_merge(const DecodeArgs& a, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+  if (a.batch * a.num_heads <= 256)
+    return launch(mla_merge_kernel<64>, dim3(kDV / 64, a.num_heads, a.batch), dim3(kMergeThreads), stream, t0, t1, a);
+  return launch(mla_merge_kernel<256>, dim3(kDV / 256, a.num_heads, a.batch), dim3(kMergeThreads), stream, t0, t1,
+                a);
+}
+
 template <int FMT, bool TILEPAGE, int NS>
 static hipError_t launch_fmt(const DecodeArgs& a, hipStream_t stream, const ProfileEvents& ev) {
   const dim3 grid(a.num_splits, a.batch, a.num_heads / 16), block(Geo<NS>::kThreads);
@@ -858,11 +865,11 @@ static hipError_t launch_fmt(const DecodeArgs& a, hipStream_t stream, const Prof
   hipError_t e = launch(mla_decode_kernel<FMT, false, TILEPAGE, NS>, grid, block, stream, ev.split_start,
                         ev.split_end, a);
   if (e != hipSuccess) return e;
-  if (a.batch * a.num_heads <= 256)
-    return launch(mla_merge_kernel<64>, dim3(kDV / 64, a.num_heads, a.batch), dim3(kMergeThreads), stream,
-                  ev.merge_start, ev.merge_end, a);
-  return launch(mla_merge_kernel<256>, dim3(kDV / 256, a.num_heads, a.batch), dim3(kMergeThreads), stream,
-                ev.merge_start, ev.merge_end, a);
+  return launch_fmt_merge(a, stream, ev.merge_start, ev.merge_end);
+}
+
+hipError_t launch_merge(const DecodeArgs& a, hipStream_t stream) {
+  return launch_fmt_merge(a, stream, nullptr, nullptr);
 }
 
 // Pages of at least a tile hold whole tiles (one descriptor per tile); shorter pages are

@@ -89,7 +89,13 @@ __global__ __launch_bounds__(64) void extend_index_kernel(ExtendArgs a) {
   int P, C, q0;
   const bool ok = extend_bounds(a, b, P, C, q0) && t >= q0 && t < q0 + C;
   if (lane == 0) a.view_lens[t] = ok ? P + (t - q0) + 1 : -1;
-  for (int k = lane; k < npp; k += 64) a.view_indices[(int64_t)t * npp + k] = b * npp + k;
+  if (a.write_pages)
+    for (int k = lane; k < npp; k += 64) a.view_indices[(int64_t)t * npp + k] = b * npp + k;
+  if (!ok && a.nan_out) {   // the tiled attention skips invalid requests: their outputs are NaN
+    float* o = a.nan_out + (int64_t)t * 16 * kDV;
+    for (int k = lane; k < 16 * kDV; k += 64) o[k] = NAN;
+    if (a.nan_lse && lane < 16) a.nan_lse[(int64_t)t * 16 + lane] = NAN;
+  }
 }
 
 hipError_t launch_extend_views(const ExtendArgs& a, hipStream_t stream) {

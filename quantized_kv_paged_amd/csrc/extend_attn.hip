@@ -1,0 +1,270 @@
+// Extend attention over the FP8 workspace with one shared K/V tile per workgroup.
+//
+// Extend (NVFP4 article on aitop.news, implementation item 2) attends every chunk token of a
+// request over the same workspace rows (prefix, then the chunk), causally.  Attending each
+// token in its own decode workgroup re-reads and re-converts every row once per token; here a
+// workgroup takes kXT consecutive chunk tokens of one request (a wave pair per token: the two
+// halves of the 576 score dims and of the 512 value dims, as in the decode kernel) and walks
+// the rows once for all of them: per tile of 32 rows, the 512 threads load the FP8 rows,
+// convert them to fp16 into an LDS tile shared by the 8 waves (rows loaded two tiles ahead,
+// converted into the second of two LDS buffers one tile ahead), and every wave reads its K
+// operands and its transposed V operands from it.
+// Token i of the request masks rows >= P + i + 1.  A single split writes out and lse;
+// several splits write decode-layout partials for the merge kernel.
+#include "device_common.h"
+#include "mlaq_kernels.h"
+
+namespace mlaq {
+
+constexpr int kXT = 4;                          // chunk tokens per workgroup
+constexpr int kXWaves = 2 * kXT;
+constexpr int kXThreads = 64 * kXWaves;         // 512
+constexpr int kXRows = 32;                      // rows per tile (two 16-row MFMA blocks)
+constexpr int kXRowB = 1280;                    // LDS bytes per tile row: 576 fp16 dims in 80 chunks
+constexpr int kXTileB = kXRows * kXRowB;        // 40 KB
+constexpr int kXSwapW = 2 * 64 * 16;            // a wave's partial scores (2 KB)
+constexpr int kXSmem = 2 * kXTileB + 2 * kXWaves * kXSwapW;   // 112 KB: one workgroup per CU
+constexpr float kXMinusBig = -3.0e38f;
+constexpr float kXSlack = 8.0f;
+static_assert(kXSmem <= 160 * 1024, "LDS");
+
+// Tile row r, 16-byte chunk c (dims 8c .. 8c+7) lives at chunk (c & ~15) | ((c & 15) ^ s(r)),
+// s(r) = x ^ 2x (mod 16), x = r mod 16: rows start on 256-byte boundaries (1280 = 5 * 256), so
+// the K-operand reads (16 rows x 4 chunks per instruction), the transposed V reads and the
+// row-major tile writes below each spread over all 64 banks (checked by enumeration).
+__device__ __forceinline__ int xswz(int r) { const int x = r & 15; return (x ^ (x << 1)) & 15; }
+__device__ __forceinline__ int xoff(int r, int c) { return r * kXRowB + 16 * ((c & ~15) | ((c & 15) ^ xswz(r))); }
+
+__global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[kXSmem];
+  const int blk = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
+  const int pi = w >> 1, dh = w & 1;             // token of the pair, dim half
+
+  // ---- request bounds (the checks of the view builder; invalid requests were given NaN there)
+  const int P = a.prefix_lens[b], q0 = a.qo_indptr[b], C = a.qo_indptr[b + 1] - q0;
+  const int p0 = a.kv_indptr[b], p1 = a.kv_indptr[b + 1];
+  const bool ok = P >= 0 && P <= a.max_prefix_len && C >= 0 && C <= a.max_chunk_len && q0 >= 0 &&
+                  q0 + C <= a.num_q && p0 >= 0 && p1 >= p0 && p1 <= a.kv_indptr[a.batch] &&
+                  (int64_t)(p1 - p0) * a.page_size >= (int64_t)P;
+  const int i0 = blk * kXT;
+  if (!ok || i0 >= C) return;                    // uniform
+  const int ci = i0 + pi;                        // this pair's chunk token
+  const bool tok = ci < C;                       // wave-uniform
+  const int t = q0 + (tok ? ci : C - 1);         // its query row (a valid one for idle pairs)
+  const int vis = tok ? P + ci + 1 : 0;          // rows it sees
+  const int rows_blk = P + min(C, i0 + kXT);     // rows any token of the block sees
+  const int tiles_all = (rows_blk + kXRows - 1) / kXRows;
+  const int tt0 = split * a.tiles_per_split;
+  const int tt1 = min(tiles_all, tt0 + a.tiles_per_split);
+  const int ntiles = max(0, tt1 - tt0);
+
+  const uint8_t* reg = a.ws_rows + (int64_t)b * a.region_rows * kD;
+  char* const tiles = smem;
+  float* const sX = reinterpret_cast<float*>(smem + 2 * kXTileB);
+
+  // tile loader: thread u of 1152 (16-byte groups) takes row u % 32, dims 16(u / 32) .. +15;
+  // rows at or past rows_blk read zeros (descriptor limit)
+  u32x4 raw[3];
+  auto load = [&](int tt) __attribute__((always_inline)) {
+    const int r0 = tt * kXRows;
+    const int nrows = max(0, min(kXRows, rows_blk - r0));
+    const BufferRsrc rs = make_rsrc(reg + (int64_t)r0 * kD, nrows * kD);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int u = tid + kXThreads * j;
+      raw[j] = u < 1152 ? buffer_load_b128(rs, (u & 31) * kD + 16 * (u >> 5)) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store = [&](int buf) __attribute__((always_inline)) {
+    char* tile = tiles + buf * kXTileB;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int u = tid + kXThreads * j;
+      if (u < 1152) {
+        const int r = u & 31, k = u >> 5;
+        u32x4 lo, hi;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const f16x2 a0 = fp8x2_to_f16<false>(raw[j][e]), a1 = fp8x2_to_f16<true>(raw[j][e]);
+          lo[2 * e] = __builtin_bit_cast(uint32_t, a0);
+          lo[2 * e + 1] = __builtin_bit_cast(uint32_t, a1);
+          const f16x2 b0 = fp8x2_to_f16<false>(raw[j][2 + e]), b1 = fp8x2_to_f16<true>(raw[j][2 + e]);
+          hi[2 * e] = __builtin_bit_cast(uint32_t, b0);
+          hi[2 * e + 1] = __builtin_bit_cast(uint32_t, b1);
+        }
+        *reinterpret_cast<u32x4*>(tile + xoff(r, 2 * k)) = lo;
+        *reinterpret_cast<u32x4*>(tile + xoff(r, 2 * k + 1)) = hi;
+      }
+    }
+  };
+
+  // this token's query half as fp16 (exact after a power-of-two prescale per head and half,
+  // folded into the score scale), k-block kb of lane (g, head l16) = dims xdim(kb) .. +7
+  auto xdim = [&](int kb) { return kb == 8 ? 512 + 32 * dh + 8 * grp : 256 * dh + 64 * (kb >> 1) + 16 * grp + 8 * (kb & 1); };
+  f16x8 qop[9];
+  float score_scale;
+  {
+    const uint16_t* qrow = a.q + ((int64_t)t * 16 + l16) * kD;
+    u32x4 qraw[9];
+#pragma unroll
+    for (int kb = 0; kb < 9; ++kb) qraw[kb] = *reinterpret_cast<const u32x4*>(qrow + xdim(kb));
+    uint32_t mx = 0;
+#pragma unroll
+    for (int kb = 0; kb < 9; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mx = max(mx, max((qraw[kb][e] & 0x7fffu) << 16, qraw[kb][e] & 0x7fff0000u));
+    const float qmax = rows_max(u2f(mx));
+    const int ex = (int)((f2u(qmax) >> 23) & 0xff) - 127;
+    const int sh = (qmax == 0.0f || ex >= 128) ? 0 : min(15 - ex, 64);
+    const float up = u2f((uint32_t)(127 + sh) << 23);
+    score_scale = a.score_scale * u2f((uint32_t)(127 - sh) << 23);
+#pragma unroll
+    for (int kb = 0; kb < 9; ++kb) {
+      f16x8 qv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qv[2 * e] = (_Float16)(u2f(qraw[kb][e] << 16) * up);
+        qv[2 * e + 1] = (_Float16)(u2f(qraw[kb][e] & 0xffff0000u) * up);
+      }
+      qop[kb] = qv;
+    }
+  }
+
+  // lane bases: K operand of k-block kb, block tb = qb ^ 16(8((kb >> 1) & 1) + (kb & 1)) +
+  // 256(kb >> 2) + 16 kXRowB tb (kb < 8), qb8 for the rope k-block; V operand of dims
+  // 256dh + 16nt + 4q of rows 16tb + 4g + i = (vrb ^ 32(nt & 7)) + 256(nt >> 3) + 16 kXRowB tb
+  const int qb = l16 * kXRowB + 16 * ((2 * grp) ^ xswz(l16)) + 512 * dh;
+  const int qb8 = l16 * kXRowB + 1024 + 16 * ((4 * dh + grp) ^ xswz(l16));
+  const int q4 = l16 & 3, vrow = 4 * grp + (l16 >> 2);
+  const int vrb = vrow * kXRowB + 16 * ((q4 >> 1) ^ xswz(vrow)) + 8 * (q4 & 1) + 512 * dh;
+
+  float m_run = kXMinusBig, l_run = 0.0f;
+  f32x4 o[16];
+#pragma unroll
+  for (int nt = 0; nt < 16; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // pipeline: tile k is in LDS buffer k & 1; the rows of tile k + 1 arrived in registers during
+  // tile k - 1 and are converted into the other buffer at the start of tile k (its last readers
+  // passed the barrier that ended tile k - 1); then the rows of tile k + 2 are loaded
+  if (ntiles > 0) {
+    load(tt0);
+    store(0);
+    if (ntiles > 1) load(tt0 + 1);
+    __syncthreads();
+  }
+  for (int k = 0; k < ntiles; ++k) {
+    const int tt = tt0 + k, buf = k & 1;
+    if (k + 1 < ntiles) {
+      store(buf ^ 1);
+      if (k + 2 < ntiles) load(tt + 2);
+    }
+    const char* tile = tiles + buf * kXTileB;
+    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int kb = 0; kb < 9; ++kb)
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const int off = kb < 8 ? ((qb ^ (16 * (8 * ((kb >> 1) & 1) + (kb & 1)))) + 256 * (kb >> 2)) : qb8;
+        const f16x8 kop = *reinterpret_cast<const f16x8*>(tile + off + 16 * kXRowB * tb);
+        sacc[tb] = mfma16x16x32(kop, qop[kb], sacc[tb]);
+      }
+    // scores of this token: lane (g, head l16) holds rows 32tt + 16tb + 4g + j
+    f32x4 sp[2];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      sp[tb] = sacc[tb] * score_scale;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (32 * tt + 16 * tb + 4 * grp + j >= vis) sp[tb][j] = -INFINITY;
+    }
+    float* const xw = sX + (buf * kXWaves + w) * (kXSwapW / 4);
+    const float* const xp = sX + (buf * kXWaves + (w ^ 1)) * (kXSwapW / 4);
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) *reinterpret_cast<f32x4*>(xw + 256 * tb + 4 * lane) = sp[tb];
+    __syncthreads();
+    float sc[8];
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const f32x4 sq = *reinterpret_cast<const f32x4*>(xp + 256 * tb + 4 * lane);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sc[4 * tb + j] = sp[tb][j] + sq[j];
+    }
+    float lmax = sc[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) lmax = fmaxf(lmax, sc[j]);
+    const float tmax = rows_max(lmax);
+    const bool grow = tmax > m_run + kXSlack;
+    if (__any(grow)) {
+      const float m_new = grow ? tmax : m_run;
+      const float alpha = fast_exp2(m_run - m_new);
+      l_run *= alpha;
+      m_run = m_new;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ai = __shfl(alpha, 4 * grp + i);
+#pragma unroll
+        for (int nt = 0; nt < 16; ++nt) o[nt][i] *= ai;
+      }
+    }
+    f16x8 pop;
+    float rsum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float pe = fast_exp2(sc[j] - m_run);
+      rsum += pe;
+      pop[j] = (_Float16)pe;
+    }
+    l_run += rows_sum(rsum);
+#pragma unroll
+    for (int nt = 0; nt < 16; ++nt) {
+      const char* pv = tile + ((vrb ^ (32 * (nt & 7))) + 256 * (nt >> 3));
+      const i16x4 lo = lds_read_tr16(pv), hi = lds_read_tr16(pv + 16 * kXRowB);
+      const i16x8 v = i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      o[nt] = mfma16x16x32(pop, __builtin_bit_cast(f16x8, v), o[nt]);
+    }
+    __syncthreads();
+  }
+
+  // ---- outputs of this token: O for heads 4g + i, dims 256dh + 16nt + l16; (m, l) for head l16
+  if (!tok) return;
+  if (a.num_splits == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * grp + i;
+      const float L = __shfl(l_run, h);
+      float f = L > 0.0f ? a.out_scale / L : 0.0f;
+      if (L != L) f = L;
+      float* dst = a.out + ((int64_t)t * 16 + h) * kDV + 256 * dh + l16;
+#pragma unroll
+      for (int nt = 0; nt < 16; ++nt) dst[16 * nt] = o[nt][i] * f;
+    }
+    if (a.lse && dh == 0 && grp == 0)
+      a.lse[(int64_t)t * 16 + l16] = l_run > 0.0f ? (m_run + __log2f(l_run)) * kLn2
+                                                   : (l_run != l_run ? l_run : -INFINITY);
+  } else {
+    const int64_t slot = (int64_t)t * a.num_splits + split;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float* dst = a.part_o + slot * (16 * kDV) + (4 * grp + i) * kDV + 256 * dh + l16;
+#pragma unroll
+      for (int nt = 0; nt < 16; ++nt) dst[16 * nt] = o[nt][i];
+    }
+    if (dh == 0 && grp == 0) {
+      a.part_ml[slot * 32 + l16] = ntiles > 0 ? m_run : -INFINITY;
+      a.part_ml[slot * 32 + 16 + l16] = l_run;
+    }
+  }
+}
+
+hipError_t launch_extend_attn(const ExtendAttnArgs& a, hipStream_t stream) {
+  const int nblk = (a.max_chunk_len + kXT - 1) / kXT;
+  hipLaunchKernelGGL(extend_attn_kernel, dim3((unsigned)nblk, (unsigned)a.batch, (unsigned)a.num_splits),
+                     dim3(kXThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+int extend_attn_tile_rows() { return kXRows; }
+int extend_attn_tokens_per_group() { return kXT; }
+
+}  // namespace mlaq
