@@ -169,3 +169,47 @@ def test_append_validation_and_workspace():
     assert s > 1
     assert qk._lib.mlaq_decode_nvfp4_append_workspace_bytes(ctypes.byref(many)) == ((2 * (s + 1) * slot + 255) // 256) * 256
     assert qk._lib.mlaq_decode_nvfp4_append_workspace_bytes(ctypes.byref(_p(num_heads=20))) == ctypes.c_size_t(-1).value
+
+
+def _ext_p(**kw):
+    d = dict(batch=2, num_heads=16, page_size=64, pool_tokens=1 << 16, num_q=64, max_prefix_len=4096,
+             max_chunk_len=32, num_splits=0, sm_scale=0.07)
+    d.update(kw)
+    return qk.extend_params(d["batch"], d["num_heads"], d["page_size"], d["pool_tokens"], d["num_q"],
+                            d["max_prefix_len"], d["max_chunk_len"], d["sm_scale"], d["num_splits"])
+
+
+def _ext(p, q=FAKE, qo=FAKE, ckv=FAKE, cs=1.0, data=FAKE, scales=FAKE, g=1.0, slots=FAKE, out=FAKE, ws=FAKE,
+         ws_bytes=1 << 34):
+    return qk._lib.mla_extend_nvfp4(ctypes.byref(p), q, qo, ckv, cs, data, scales, g, FAKE, FAKE, FAKE, slots, out,
+                                    FAKE, ws, ws_bytes, None)
+
+
+def test_extend_validation_and_workspace():
+    p = _ext_p()
+    assert _ext(_ext_p(num_heads=8)) == ERR_SHAPE
+    assert _ext(_ext_p(num_q=70000)) == ERR_SHAPE
+    assert _ext(_ext_p(max_prefix_len=-1)) == ERR_SHAPE
+    assert _ext(_ext_p(max_chunk_len=0)) == ERR_SHAPE              # num_q > 0 needs a chunk
+    assert _ext(_ext_p(page_size=48)) == ERR_SHAPE
+    assert _ext(_ext_p(pool_tokens=0)) == ERR_SHAPE
+    assert _ext(p, cs=0.0) == ERR_VALUE
+    assert _ext(p, g=float("inf")) == ERR_VALUE
+    assert _ext(p, q=None) == ERR_NULL
+    assert _ext(p, slots=None) == ERR_NULL
+    assert _ext(p, ckv=FAKE + 8) == ERR_ALIGN
+    assert _ext(p, slots=FAKE + 4) == ERR_ALIGN
+    assert _ext(p, ws=None) == ERR_NULL
+    need = qk.mlaq_extend_workspace_bytes(p)
+    assert _ext(p, ws_bytes=need - 1) == ERR_WORKSPACE
+    assert _ext(p, ws=FAKE + 16) == ERR_ALIGN
+    assert _ext(_ext_p(num_q=0), q=None, qo=None, ckv=None) == 0    # nothing to do
+    # workspace: one FP8 region of round_up(prefix + chunk, 64) rows per request, the per-token
+    # views, then the partials of the KV splits (16 heads: the shared-tile kernel's splits)
+    region = -(-(4096 + 32) // 64) * 64
+    s = qk._lib.mlaq_extend_num_splits(ctypes.byref(p))
+    assert s >= 1
+    a256 = lambda x: -(-x // 256) * 256
+    base = a256(2 * region * 576) + a256(64 * (region // 64) * 4) + a256(64 * 4) + a256(65 * 4)
+    assert need == base + (a256(64 * s * (16 * 512 * 4 + 32 * 4)) if s > 1 else 0)
+    assert qk._lib.mlaq_extend_workspace_bytes(ctypes.byref(_ext_p(num_heads=20))) == ctypes.c_size_t(-1).value
