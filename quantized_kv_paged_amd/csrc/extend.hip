@@ -31,42 +31,60 @@ __device__ __forceinline__ bool extend_bounds(const ExtendArgs& a, int b, int& P
          p0 >= 0 && p1 >= p0 && p1 <= a.kv_indptr[a.batch] && (int64_t)(p1 - p0) * a.page_size >= (int64_t)P;
 }
 
-// one thread per (row of the region, 16-value block): grid (ceil(region_rows * 36 / 256), batch)
+// one thread per (row of the region, group of 64 dims = 4 blocks): grid
+// (ceil(region_rows * 9 / 256), batch); 32 code bytes + 4 scale bytes in, 64 FP8 bytes out
 __global__ __launch_bounds__(256) void extend_gather_kernel(ExtendArgs a) {
   const int b = blockIdx.y;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (gid >= (int64_t)a.region_rows * 36) return;
-  const int r = (int)(gid / 36), k = (int)(gid - (int64_t)r * 36);
+  if (gid >= (int64_t)a.region_rows * 9) return;
+  const int r = (int)(gid / 9), k4 = (int)(gid - (int64_t)r * 9);
   int P, C, q0;
   if (!extend_bounds(a, b, P, C, q0) || r >= P + C) return;
-  u32x4* dst = reinterpret_cast<u32x4*>(a.ws_rows + ((int64_t)b * a.region_rows + r) * kD + 16 * k);
+  u32x4* dst = reinterpret_cast<u32x4*>(a.ws_rows + ((int64_t)b * a.region_rows + r) * kD + 64 * k4);
   if (r >= P) {
-    *dst = *reinterpret_cast<const u32x4*>(a.chunk_kv + (int64_t)(q0 + r - P) * kD + 16 * k);
+    const u32x4* src = reinterpret_cast<const u32x4*>(a.chunk_kv + (int64_t)(q0 + r - P) * kD + 64 * k4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dst[j] = src[j];
     return;
   }
   const int page = a.kv_indices[a.kv_indptr[b] + (r >> a.page_shift)];
   const int64_t row = ((int64_t)page << a.page_shift) + (r & (a.page_size - 1));
   if (page < 0 || row >= a.pool_tokens) {
-    *dst = u32x4{0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dst[j] = u32x4{0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu, 0x7f7f7f7fu};
     return;
   }
-  const u32x2 d = *reinterpret_cast<const u32x2*>(a.kv_data + row * kNvData + 8 * k);
-  const float s = fp8x2_to_f32<false>((uint32_t)a.kv_scales[row * kNvScale + k])[0];
-  uint32_t o[4];
+  const u32x4* cp = reinterpret_cast<const u32x4*>(a.kv_data + row * kNvData + 32 * k4);
+  const u32x4 d0 = cp[0], d1 = cp[1];
+  const uint32_t sw = *reinterpret_cast<const uint32_t*>(a.kv_scales + row * kNvScale + 4 * k4);
+  const uint32_t codes[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const f32x2 c0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d[h], 1.0f, 0);
-    const f32x2 c1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d[h], 1.0f, 1);
-    const f32x2 c2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d[h], 1.0f, 2);
-    const f32x2 c3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d[h], 1.0f, 3);
-    const float c[8] = {c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
-    uint32_t e[8];
+  for (int blk = 0; blk < 4; ++blk) {          // block 4 k4 + blk: code words 2 blk, 2 blk + 1
+    const float s = fp8x2_to_f32<false>((sw >> (8 * blk)) & 0xffu)[0];
+    uint32_t o[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) e[i] = f32_to_e4m3_rne_sat(((c[i] * s) * a.global_scale) / a.chunk_scale);
-    o[2 * h] = e[0] | (e[1] << 8) | (e[2] << 16) | (e[3] << 24);
-    o[2 * h + 1] = e[4] | (e[5] << 8) | (e[6] << 16) | (e[7] << 24);
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t cw = codes[2 * blk + h];
+      const f32x2 c0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 0);
+      const f32x2 c1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 1);
+      const f32x2 c2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 2);
+      const f32x2 c3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 3);
+      const float c[8] = {c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = (c[i] * s) * a.global_scale;
+      if (a.chunk_scale != 1.0f) {   // uniform; x / 1 == x, so the common case skips the divisions
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = v[i] / a.chunk_scale;
+      }
+      uint32_t e[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) e[i] = f32_to_e4m3_rne_sat(v[i]);
+      o[2 * h] = e[0] | (e[1] << 8) | (e[2] << 16) | (e[3] << 24);
+      o[2 * h + 1] = e[4] | (e[5] << 8) | (e[6] << 16) | (e[7] << 24);
+    }
+    dst[blk] = u32x4{o[0], o[1], o[2], o[3]};
   }
-  *dst = u32x4{o[0], o[1], o[2], o[3]};
 }
 
 // one workgroup of 64 threads per query token t (grid num_q): its request (binary search in
@@ -100,7 +118,7 @@ __global__ __launch_bounds__(64) void extend_index_kernel(ExtendArgs a) {
 
 hipError_t launch_extend_views(const ExtendArgs& a, hipStream_t stream) {
   if (a.region_rows > 0) {
-    const int64_t n = (int64_t)a.region_rows * 36;
+    const int64_t n = (int64_t)a.region_rows * 9;
     hipLaunchKernelGGL(extend_gather_kernel, dim3((unsigned)((n + 255) / 256), (unsigned)a.batch), dim3(256), 0,
                        stream, a);
     hipError_t e = hipGetLastError();

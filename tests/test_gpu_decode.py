@@ -70,6 +70,16 @@ def test_32_heads():
     _run(c, splits=(0, 3), tag="H64 nvfp4")
 
 
+def test_limits_128_heads_1024_page_1024_splits():
+    """The largest shapes the ABI accepts: 128 heads (8 head groups), 1,024-token pages, 1,024 splits."""
+    c = build_case("fp8", [300, 77], 16, seed=18, heads=128)
+    _run(c, splits=(0, 2), tag="H128")
+    c = build_case("nvfp4", [3000, 1500], 1024, seed=19, outlier_p=0.01, extra_pages=1)
+    _run(c, splits=(0, 1), tag="P1024 nvfp4")
+    c = build_case("nvfp4", [40000], 64, seed=20, outlier_p=0.01, extra_pages=1)
+    _run(c, splits=(1024,), tag="1024 splits")
+
+
 def test_page_placement_is_bitwise_invariant():
     """The same logical KV under two different physical page layouts gives identical bits."""
     c1 = build_case("fp8", [700, 130], 16, seed=21, extra_pages=9)
