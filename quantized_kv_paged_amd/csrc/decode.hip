@@ -620,10 +620,18 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
     float rsum = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4 * kBlocks; ++j) {
+      // the sum takes the rounded probabilities the products use, so that the output is a
+      // convex combination of value rows (rows with equal values reproduce them exactly)
       const float pe = fast_exp2(sc[j] - m_run);
-      rsum += pe;
       if constexpr (FMT == FMT_BF16) pop[j] = (__bf16)pe;
       else pop[j] = (_Float16)pe;
+    }
+#pragma unroll
+    for (int j = 0; j < 4 * kBlocks; j += 2) {    // sum of the rounded pairs, one dot2 per pair
+      if constexpr (FMT == FMT_BF16)
+        rsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pop[j], pop[j + 1]}, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, rsum, false);
+      else
+        rsum = __builtin_amdgcn_fdot2(f16x2{pop[j], pop[j + 1]}, f16x2{(_Float16)1.0f, (_Float16)1.0f}, rsum, false);
     }
     l_run += rows_sum(rsum);
     // O += P V: 16 dims per product, K = this group's 32 tokens.  The operands are read in

@@ -211,10 +211,11 @@ __global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArg
     float rsum = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float pe = fast_exp2(sc[j] - m_run);
-      rsum += pe;
-      pop[j] = (_Float16)pe;
+      pop[j] = (_Float16)fast_exp2(sc[j] - m_run);
     }
+#pragma unroll
+    for (int j = 0; j < 8; j += 2)                 // the rounded probabilities the products use
+      rsum = __builtin_amdgcn_fdot2(f16x2{pop[j], pop[j + 1]}, f16x2{(_Float16)1.0f, (_Float16)1.0f}, rsum, false);
     l_run += rows_sum(rsum);
 #pragma unroll
     for (int nt = 0; nt < 16; ++nt) {

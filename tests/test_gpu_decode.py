@@ -105,7 +105,8 @@ def test_fp8_and_nvfp4_agree_on_shared_values():
     shapes (two softmax streams per workgroup for FP8, one for NVFP4), so probabilities are
     rounded to fp16 against different running maxima and sums are grouped differently: the
     outputs must agree to that rounding (about 2^-11 relative), far inside the oracle
-    tolerance."""
+    tolerance.  The softmax sums add the rounded probabilities (each within 2^-12 of the
+    exact one), so the two lse agree to 2^-12 in the sum, about 2.4e-4 in the log."""
     c = build_case("fp8", [333, 1024], 64, seed=22)
     rng = np.random.default_rng(6)
     codes = rng.integers(0, 16, size=c.fp8_pool.shape, dtype=np.uint8)
@@ -121,7 +122,7 @@ def test_fp8_and_nvfp4_agree_on_shared_values():
         o1, l1 = gpu_decode(c, Device(c), num_splits=s)
         o2, l2 = gpu_decode(nv, Device(nv), num_splits=s)
         assert np.abs(o1 - o2).max() <= 1e-3 * max(1.0, np.abs(o1).max()), s
-        assert np.abs(l1 - l2).max() <= 1e-4, s
+        assert np.abs(l1 - l2).max() <= 5e-4, s
     ref_out, ref_lse = oracle_decode(nv)
     assert_parity(o2, l2, ref_out, ref_lse, tag="shared values")
 
