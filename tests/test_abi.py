@@ -127,6 +127,8 @@ def test_split_planning_and_workspace():
             slots = w.batch * s * (w.heads // 16)
             assert ws == ((slots * (16 * 512 * 4 + 32 * 4) + 255) // 256) * 256
         assert qk.mlaq_decode_num_splits(p, qk.MLAQ_BF16) == expect[name][0]
+        slots = w.batch * expect[name][0] * (w.heads // 16)
+        assert qk.mlaq_decode_workspace_bytes(p, qk.MLAQ_BF16) == ((slots * (16 * 512 * 4 + 32 * 4) + 255) // 256) * 256
     for fmt in (qk.MLAQ_FP8_E4M3, qk.MLAQ_NVFP4, qk.MLAQ_BF16):
         assert qk.mlaq_decode_num_splits(_p(max_kv_len=32), fmt) == 1
         assert qk.mlaq_decode_workspace_bytes(_p(max_kv_len=32), fmt) == 0
