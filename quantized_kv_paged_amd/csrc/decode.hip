@@ -358,8 +358,6 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
   constexpr int kThreads = Geo<NS>::kThreads, kSwap = Geo<NS>::kSwap, kSmem = Geo<NS>::kSmem;
   constexpr int kMLOff = Geo<NS>::kMLOff;
   typedef typename OpType<FMT>::type Op;
-  // raw tiles in flight per wave: two for the 8-bit and 4-bit pools, one for the 16-bit pool
-  constexpr int kBufs = 1;
   // the waves' value tiles (4 x 16 KB) and the partial-score swap buffers (2 x 4 x 2 KB); at
   // the end of the chunk, the streams' output buffer of one dim half and their (m, l)
   __shared__ __attribute__((aligned(16))) char smem[kSmem];
@@ -413,8 +411,10 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
   const int my_tok = 16 * kBlocks * tg + l16;
   char* const vt = smem + w * kWaveV;
   float* const sX = reinterpret_cast<float*>(smem + kSwap);
-  RawTile<FMT> rawA[kBlocks], rawB[kBlocks];
-  int stA[kBlocks], stB[kBlocks];
+  // one raw tile per wave: refilled with the next tile's rows as soon as it is converted (two
+  // in flight did not fit the registers next to the output accumulator)
+  RawTile<FMT> rawA[kBlocks];
+  int stA[kBlocks];
   // prologue, ordered for the in-order load counter: the first two page-table batches, this
   // wave's half of the query rows, then the first tiles' rows; the query is converted while
   // those are in flight
@@ -459,9 +459,6 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
     for (int kb = 0; kb < 9; ++kb) qraw[kb] = *reinterpret_cast<const u32x4*>(qrow + kb_dim<FMT>(dh, kb, grp));
   }
   fetch(rawA, stA, t_begin);
-  if constexpr (kBufs == 2) {
-    if (ntiles > 1) fetch(rawB, stB, t_begin + kTile);
-  }
 
   Op qop[9];
   float score_scale = a.score_scale;
@@ -518,7 +515,7 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
   const int vrb = vrow * kVRow + 16 * ((q4 >> 1) ^ vswz(vrow)) + 8 * (q4 & 1);
 
   // One tile: partial S^T of this wave's dim half for its two token blocks (value dims to
-  // LDS), refill of the raw buffer with the tile kBufs ahead, swap of partial scores with the
+  // LDS), refill of the raw buffer with the next tile, swap of partial scores with the
   // pair partner, online softmax of the stream, O += P V over the wave's dim half.
   auto compute = [&](RawTile<FMT>(&cur)[kBlocks], int(&st)[kBlocks], int t0, int buf, bool more)
                      __attribute__((always_inline)) {
@@ -539,13 +536,13 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
     MLAQ_QK_STEP(0) MLAQ_QK_STEP(1) MLAQ_QK_STEP(2) MLAQ_QK_STEP(3) MLAQ_QK_STEP(4)
     MLAQ_QK_STEP(5) MLAQ_QK_STEP(6) MLAQ_QK_STEP(7) MLAQ_QK_STEP(8)
 #undef MLAQ_QK_STEP
-    // the raw tile is converted: its registers take the loads of the tile kBufs ahead, which
+    // the raw tile is converted: its registers take the loads of the next tile, which
     // are in flight during this tile's softmax and PV and the next tiles
     // wave priority: the conversion and QK stretch runs at the highest priority, so that
     // the other wave of the SIMD (of another workgroup) fills its gaps only while this one
     // waits; the score swap runs at 1, the softmax and PV (latency-bound) at 0
     __builtin_amdgcn_s_setprio(1);
-    if (more) fetch(cur, st, t0 + kBufs * kTile);
+    if (more) fetch(cur, st, t0 + kTile);
     // lane: head l16, tokens 32tg + 16tb + 4grp + i
     f32x4 sp[kBlocks];
 #pragma unroll
@@ -652,18 +649,8 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
   };
 
   __builtin_amdgcn_s_setprio(3);
-  // ---- tile loop: kBufs raw buffers per wave, each refilled (with the tile kBufs ahead) as
-  //      soon as its tile is converted.  The score swap buffers alternate with the tiles.
-  if constexpr (kBufs == 1) {
-    for (int k = 0; k < ntiles; ++k) compute(rawA, stA, t_begin + k * kTile, k & 1, k + 1 < ntiles);
-  } else {
-    for (int k = 0; k < ntiles; k += 2) {
-      const int t0 = t_begin + k * kTile;
-      compute(rawA, stA, t0, 0, k + 2 < ntiles);
-      if (k + 1 >= ntiles) break;
-      compute(rawB, stB, t0 + kTile, 1, k + 3 < ntiles);
-    }
-  }
+  // ---- tile loop; the score swap buffers alternate with the tiles
+  for (int k = 0; k < ntiles; ++k) compute(rawA, stA, t_begin + k * kTile, k & 1, k + 1 < ntiles);
 
   // ---- merge the token-group streams in LDS.  Stream tg: running max m_tg, sum l_tg;
   //      weights w_tg = 2^(m_tg - M), M = max_tg m_tg; L = sum_tg w_tg l_tg.  The weighted
