@@ -191,6 +191,10 @@ mlaq_status extend_layout(const mlaq_extend_params* p, ExtendLayout& L) {
   const int64_t span = (int64_t)p->max_prefix_len + p->max_chunk_len;
   L.region_rows = (int)((span + mlaq::kExtendPage - 1) / mlaq::kExtendPage * mlaq::kExtendPage);
   L.npp = L.region_rows / mlaq::kExtendPage;
+  // the per-token views are int32 page tables over batch regions of npp pages
+  if ((int64_t)p->num_q * L.npp >= ((int64_t)1 << 31) || (int64_t)p->batch * L.npp >= ((int64_t)1 << 31))
+    return fail(MLAQ_ERR_SHAPE, "extend views too large: num_q %d / batch %d x %d pages per region", p->num_q,
+                p->batch, L.npp);
   L.dp.batch = p->num_q;
   L.dp.num_heads = p->num_heads;
   L.dp.page_size = mlaq::kExtendPage;

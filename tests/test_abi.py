@@ -195,6 +195,7 @@ def test_extend_validation_and_workspace():
     assert _ext(_ext_p(max_chunk_len=0)) == ERR_SHAPE              # num_q > 0 needs a chunk
     assert _ext(_ext_p(page_size=48)) == ERR_SHAPE
     assert _ext(_ext_p(pool_tokens=0)) == ERR_SHAPE
+    assert _ext(_ext_p(num_q=65535, max_prefix_len=1 << 25, max_chunk_len=1 << 25)) == ERR_SHAPE   # int32 views
     assert _ext(p, cs=0.0) == ERR_VALUE
     assert _ext(p, g=float("inf")) == ERR_VALUE
     assert _ext(p, q=None) == ERR_NULL
