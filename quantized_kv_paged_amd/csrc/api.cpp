@@ -395,9 +395,9 @@ mlaq_status mla_extend_nvfp4(const mlaq_extend_params* p, const uint16_t* q, con
     x.out_scale = chunk_scale;
     const mlaq::ProfileEvents ev = g_events;
     g_events = mlaq::ProfileEvents();
-    if (ev.split_start) hipEventRecord(ev.split_start, stream);
+    if (ev.split_start) (void)hipEventRecord(ev.split_start, stream);
     e = mlaq::launch_extend_attn(x, stream);
-    if (ev.split_end) hipEventRecord(ev.split_end, stream);
+    if (ev.split_end) (void)hipEventRecord(ev.split_end, stream);
     if (e != hipSuccess) return fail(MLAQ_ERR_LAUNCH, "extend attention launch failed: %s", hipGetErrorString(e));
     if (L.tsplits > 1) {
       mlaq::DecodeArgs m{};
@@ -414,9 +414,9 @@ mlaq_status mla_extend_nvfp4(const mlaq_extend_params* p, const uint16_t* q, con
       m.num_splits = L.tsplits;
       m.part_splits = L.tsplits;
       m.out_scale = chunk_scale;
-      if (ev.merge_start) hipEventRecord(ev.merge_start, stream);
+      if (ev.merge_start) (void)hipEventRecord(ev.merge_start, stream);
       e = mlaq::launch_merge(m, stream);
-      if (ev.merge_end) hipEventRecord(ev.merge_end, stream);
+      if (ev.merge_end) (void)hipEventRecord(ev.merge_end, stream);
       if (e != hipSuccess) return fail(MLAQ_ERR_LAUNCH, "extend merge launch failed: %s", hipGetErrorString(e));
     }
   } else {

@@ -50,7 +50,6 @@ constexpr int kBlocks = 2;                 // 16-token MFMA blocks per wave per 
 constexpr int kVRow = 512;                 // bytes per LDS value row of a wave (its 256 fp16 dims)
 constexpr int kWaveV = 16 * kBlocks * kVRow;       // a wave's value tile (16 KB)
 constexpr int kSwapW = kBlocks * 64 * 16;          // bytes of a wave's partial scores (2 KB)
-constexpr int kORow = 260;                 // fp32 row stride of the end-of-chunk merge buffer (padded)
 
 // Workgroup geometry for NS online-softmax streams (token groups): 2 NS waves (one per
 // (stream, dim half)), tiles of 32 NS tokens, LDS = value tiles + double-buffered score swap.
@@ -61,8 +60,6 @@ template <int NS> struct Geo {
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kSwap = kWaves * kWaveV;                 // byte offset of the swap buffers
   static constexpr int kSmem = kSwap + 2 * kWaves * kSwapW;     // 40 KB (NS = 1) or 80 KB (NS = 2)
-  static constexpr int kMLOff = kSmem - NS * 2 * 16 * 4;        // byte offset of the streams' (m, l)
-  static_assert(NS * 16 * kORow * 4 <= kMLOff, "merge buffer overlaps the (m, l) table");
   static_assert(kTile == decode_tile(NS), "tile size shared with the host planner");
   static_assert(decode_groups_per_cu(NS) * kSmem <= 160 * 1024, "resident workgroups per CU");
 };
@@ -356,10 +353,9 @@ template <int FMT, bool DIRECT, bool TILEPAGE, int NS>
 __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(DecodeArgs a) {
   constexpr int kStreams = Geo<NS>::kStreams, kTile = Geo<NS>::kTile, kWaves = Geo<NS>::kWaves;
   constexpr int kThreads = Geo<NS>::kThreads, kSwap = Geo<NS>::kSwap, kSmem = Geo<NS>::kSmem;
-  constexpr int kMLOff = Geo<NS>::kMLOff;
   typedef typename OpType<FMT>::type Op;
-  // the waves' value tiles (4 x 16 KB) and the partial-score swap buffers (2 x 4 x 2 KB); at
-  // the end of the chunk, the streams' output buffer of one dim half and their (m, l)
+  // the waves' value tiles (kWaves x 16 KB) and the partial-score swap buffers (2 x kWaves x
+  // 2 KB); at the end of the chunk, the waves' accumulators and the streams' (m, l)
   __shared__ __attribute__((aligned(16))) char smem[kSmem];
 
   const int split = blockIdx.x, b = blockIdx.y, hg = blockIdx.z;
@@ -652,76 +648,73 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
   // ---- tile loop; the score swap buffers alternate with the tiles
   for (int k = 0; k < ntiles; ++k) compute(rawA, stA, t_begin + k * kTile, k & 1, k + 1 < ntiles);
 
-  // ---- merge the token-group streams in LDS.  Stream tg: running max m_tg, sum l_tg;
-  //      weights w_tg = 2^(m_tg - M), M = max_tg m_tg; L = sum_tg w_tg l_tg.  The weighted
-  //      outputs of one dim half at a time go through a [tg][head][256] buffer (rows padded to
-  //      kORow floats so the four lane groups of a write hit different banks).
-  __syncthreads();                                   // all value-tile and swap reads are done
-  float* const sML = reinterpret_cast<float*>(smem + kMLOff);   // [tg][m, l][head]
-  if (dh == 0 && grp == 0) { sML[tg * 32 + l16] = m_run; sML[tg * 32 + 16 + l16] = l_run; }
-  __syncthreads();
-  float wgt[4];
+  // ---- end of the chunk: merge of the token-group streams.  Stream tg: running max m_tg, sum
+  //      l_tg; weights w_tg = 2^(m_tg - M), M = max_tg m_tg; L = sum_tg w_tg l_tg.
+  //      Each wave leaves its accumulator in its own value tile, which no other wave reads and
+  //      whose last reads (the products of the last tile) are done, as fp32 rows [head][256]
+  //      with the 16-byte chunks of row h XORed by 4((h >> 2) & 3) (the lane groups of a write
+  //      hit different banks, the 64 lanes of a row read hit 64 chunks); its (m, l) go to its
+  //      slot of the swap buffer the last tile did not use (every wave read that buffer for the
+  //      last time before the last tile's barrier).  With one stream a wave then reads back
+  //      its own rows (in order within the wave); with two, one barrier, then wave (tg, dh)
+  //      writes heads 8tg .. 8tg + 7 of dim half dh from both streams' rows.
+  {
+    float* const dump = reinterpret_cast<float*>(vt);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int h = 4 * grp + i;
-    float M = kMinusBig;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int g = 0; g < kStreams; ++g) M = fmaxf(M, sML[g * 32 + h]);
-    wgt[i] = fast_exp2(sML[tg * 32 + h] - M);
-  }
-  // thread -> dims 4(tid % 64) .. +3 of the half, heads tid / 64 + kWaves j
-  constexpr int kHeadsPerThread = 16 / kWaves;
-  const int dq = 4 * (tid & 63);
-  float Mh[kHeadsPerThread], Lh[kHeadsPerThread];
-#pragma unroll
-  for (int j = 0; j < kHeadsPerThread; ++j) {
-    const int h = (tid >> 6) + kWaves * j;
-    float M = kMinusBig;
-#pragma unroll
-    for (int g = 0; g < kStreams; ++g) M = fmaxf(M, sML[g * 32 + h]);
-    float Lsum = 0.0f;
-#pragma unroll
-    for (int g = 0; g < kStreams; ++g) Lsum += fast_exp2(sML[g * 32 + h] - M) * sML[g * 32 + 16 + h];
-    Mh[j] = M;
-    Lh[j] = Lsum;
-  }
-  float* const sO = reinterpret_cast<float*>(smem);
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {
-    if (dh == half) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float* dst = sO + (tg * 16 + 4 * grp + i) * kORow + l16;
-#pragma unroll
-        for (int nt = 0; nt < 16; ++nt) dst[16 * nt] = o[nt][i] * wgt[i];
-      }
+      for (int nt = 0; nt < 16; ++nt) dump[(4 * grp + i) * 256 + 16 * (nt ^ grp) + l16] = o[nt][i];
+    if constexpr (kStreams > 1) {
+      float* const tab = sX + ((ntiles & 1) * kWaves + w) * (kSwapW / 4);
+      if (grp == 0) { tab[l16] = m_run; tab[16 + l16] = l_run; }
+      __syncthreads();
+    } else {
+      __builtin_amdgcn_wave_barrier();
     }
-    __syncthreads();
+  }
+  constexpr int kHeadsPerWave = 16 / kStreams;
 #pragma unroll
-    for (int j = 0; j < kHeadsPerThread; ++j) {
-      const int h = (tid >> 6) + kWaves * j;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < kHeadsPerWave; ++j) {
+    const int h = kHeadsPerWave * tg + j;
+    float mg[kStreams], lg[kStreams];
 #pragma unroll
-      for (int g = 0; g < kStreams; ++g) acc += *reinterpret_cast<const f32x4*>(sO + (g * 16 + h) * kORow + dq);
-      const int d = 256 * half + dq;
-      if constexpr (DIRECT) {
-        const float Lsum = Lh[j];
-        float f = Lsum > 0.0f ? a.out_scale / Lsum : 0.0f;
-        if (Lsum != Lsum) f = Lsum;   // NaN stays NaN
-        *reinterpret_cast<f32x4*>(a.out + ((int64_t)b * H + hbase + h) * kDV + d) = acc * f;
-        if (a.lse && half == 0 && (tid & 63) == 0)
-          a.lse[(int64_t)b * H + hbase + h] =
-              Lsum > 0.0f ? (Mh[j] + __log2f(Lsum)) * kLn2 : (Lsum != Lsum ? Lsum : -INFINITY);
+    for (int g = 0; g < kStreams; ++g) {
+      if constexpr (kStreams == 1) {
+        mg[g] = u2f((uint32_t)__builtin_amdgcn_readlane((int)f2u(m_run), h));   // lane h holds head h
+        lg[g] = u2f((uint32_t)__builtin_amdgcn_readlane((int)f2u(l_run), h));
       } else {
-        const int64_t slot = ((int64_t)b * a.part_splits + split) * (H / 16) + hg;
-        *reinterpret_cast<f32x4*>(a.part_o + slot * (16 * kDV) + h * kDV + d) = acc;
-        if (half == 0 && (tid & 63) == 0) {
-          a.part_ml[slot * 32 + h] = Mh[j];
-          a.part_ml[slot * 32 + 16 + h] = Lh[j];
-        }
+        const float* tab = sX + ((ntiles & 1) * kWaves + g) * (kSwapW / 4);
+        mg[g] = tab[h];
+        lg[g] = tab[16 + h];
       }
     }
-    if (half == 0) __syncthreads();                  // buffer reads done before the second half
+    float M = kMinusBig;
+#pragma unroll
+    for (int g = 0; g < kStreams; ++g) M = fmaxf(M, mg[g]);
+    float Lsum = 0.0f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int g = 0; g < kStreams; ++g) {
+      const float wg = fast_exp2(mg[g] - M);
+      Lsum += wg * lg[g];
+      const float* rows = reinterpret_cast<const float*>(smem + (g + kStreams * dh) * kWaveV);
+      acc += *reinterpret_cast<const f32x4*>(rows + h * 256 + 4 * (lane ^ (4 * ((h >> 2) & 3)))) * wg;
+    }
+    const int d = 256 * dh + 4 * lane;
+    if constexpr (DIRECT) {
+      float f = Lsum > 0.0f ? a.out_scale / Lsum : 0.0f;
+      if (Lsum != Lsum) f = Lsum;   // NaN stays NaN
+      *reinterpret_cast<f32x4*>(a.out + ((int64_t)b * H + hbase + h) * kDV + d) = acc * f;
+      if (a.lse && dh == 0 && lane == 0)
+        a.lse[(int64_t)b * H + hbase + h] = Lsum > 0.0f ? (M + __log2f(Lsum)) * kLn2 : (Lsum != Lsum ? Lsum : -INFINITY);
+    } else {
+      const int64_t slot = ((int64_t)b * a.part_splits + split) * (H / 16) + hg;
+      *reinterpret_cast<f32x4*>(a.part_o + slot * (16 * kDV) + h * kDV + d) = acc;
+      if (dh == 0 && lane == 0) {
+        a.part_ml[slot * 32 + h] = M;
+        a.part_ml[slot * 32 + 16 + h] = Lsum;
+      }
+    }
   }
   if constexpr (FMT == FMT_NVFP4) {
     if (app_here) append_partial<kThreads>(a, b, hg, L, p0, smem);
