@@ -107,6 +107,38 @@ def timed_steps(step, n_layers, steps, warmup, hip, torch, profile=True):
     return total, split, merge, total2
 
 
+PROBE_BYTES = 4 << 30                # 16x the 256 MB Infinity Cache: every pass streams from HBM
+PROBE_BLOCKS = (16384, 32768, 65536)  # 256-thread workgroups per launch; the best is reported
+
+
+def read_probe(qk, torch, split_gbs, reps=10):
+    """Measured HBM read ceiling: the library's streaming-read probe over a 4 GiB buffer, for
+    each block count reps back-to-back passes after 3 untimed ones; the best rate is reported
+    and the split kernel's KV-read rate is also given as a fraction of it."""
+    buf = torch.empty(PROBE_BYTES, dtype=torch.uint8, device="cuda")
+    best = None
+    for blocks in PROBE_BLOCKS:
+        parts = torch.empty((blocks, 16), dtype=torch.uint8, device="cuda")
+        for _ in range(3):
+            qk.read_probe(buf, blocks, parts)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(reps):
+            qk.read_probe(buf, blocks, parts)
+        end.record()
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(end) / reps
+        if best is None or ms < best[0]:
+            best = (ms, blocks)
+    del buf
+    ms, blocks = best
+    gbs = PROBE_BYTES / (ms * 1e-3) / 1e9
+    return {"bytes": PROBE_BYTES, "blocks": blocks, "ms_per_pass": round(ms, 4), "gbs": round(gbs, 1),
+            "frac_of_nominal": round(gbs / HBM_PEAK_GBS, 4),
+            "split_kernel_frac_of_probe": round(split_gbs / gbs, 4)}
+
+
 def pmc_traffic(kernel_tag: str, launches_bytes: float):
     """HBM bytes per launch from committed rocprofv3 counter summaries, if they were taken on
     the current kernel source; else None."""
@@ -279,6 +311,9 @@ def main():
                      "traffic": pmc_traffic(kernel_tag, kv_bytes), "kernel": "mla_decode_kernel",
                      "bytes_per_launch": kv_bytes},
     }
+
+    if not args.no_extras:
+        res["read_probe"] = read_probe(qk, torch, achieved)
 
     if args.copy_calibration:
         # a plain copy kernel of known size: its FETCH_SIZE / WRITE_SIZE per dispatch give the

@@ -207,6 +207,16 @@ mlaq_status kv_dequantize(mlaq_format src_format, const uint8_t* kv_data, const 
 mlaq_status mlaq_set_profile_events(hipEvent_t split_start, hipEvent_t split_end, hipEvent_t merge_start,
                                     hipEvent_t merge_end);
 
+/* Measurement aid, not part of the attention path: a streaming read of `bytes` bytes of buf
+ * (a multiple of 16; buf and partials 16-byte aligned) with nontemporal 16-byte loads by
+ * `num_blocks` workgroups of 256 threads, grid-stride.  Block k writes the XOR of the 16-byte
+ * words it read to partials[16k .. 16k+15], so the XOR of all partials is the XOR of all
+ * words of the buffer.  Timed over a buffer far larger than the 256 MB Infinity Cache, it gives
+ * the HBM read bandwidth this device actually reaches, the measured ceiling reported beside
+ * the nominal 8 TB/s.  Errors: bad size or block count (MLAQ_ERR_SHAPE), NULL pointers,
+ * misalignment, launch failure. */
+mlaq_status mlaq_read_probe(const void* buf, int64_t bytes, void* partials, int32_t num_blocks, hipStream_t stream);
+
 /* (host) Message for the last non-OK status returned on this thread ("" if none). */
 const char* mlaq_last_error(void);
 

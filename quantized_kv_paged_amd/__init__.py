@@ -58,6 +58,7 @@ _SIGS = {
     "kv_quantize_nvfp4": ([_vp, ctypes.c_int, _f32, _i64, _vp, _vp, _vp, _i64, _f32, _vp], ctypes.c_int),
     "kv_dequantize": ([ctypes.c_int, _vp, _vp, _f32, _vp, _i64, _i64, ctypes.c_int, _vp, _vp], ctypes.c_int),
     "mlaq_set_profile_events": ([_vp, _vp, _vp, _vp], ctypes.c_int),
+    "mlaq_read_probe": ([_vp, _i64, _vp, _i32, _vp], ctypes.c_int),
     "mlaq_last_error": ([], ctypes.c_char_p),
     "mlaq_version": ([], ctypes.c_char_p),
 }
@@ -246,7 +247,17 @@ def kv_dequantize(src_format, kv_data, kv_scales, scale, dst_format, *, rows=Non
     return dst
 
 
+def read_probe(buf, num_blocks=2048, partials=None, stream=None):
+    """Streaming read of the device tensor buf (a measurement aid).  Returns the uint8
+    [num_blocks, 16] per-block XORs of the 16-byte words read."""
+    if partials is None:
+        partials = torch.empty((num_blocks, 16), dtype=torch.uint8, device=buf.device)
+    _check(_lib.mlaq_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(partials), num_blocks,
+                                _stream(stream)))
+    return partials
+
+
 __all__ = ["mla_decode_fp8", "mla_decode_nvfp4", "mla_decode_nvfp4_append", "mla_decode_bf16", "mla_extend_nvfp4",
            "extend_params", "mlaq_extend_workspace_bytes", "kv_quantize_nvfp4", "kv_dequantize",
            "mlaq_decode_num_splits", "mlaq_decode_workspace_bytes", "decode_params", "alloc_workspace",
-           "MlaqError", "version", "last_error", "EXPORTS", "LIB_PATH"]
+           "read_probe", "MlaqError", "version", "last_error", "EXPORTS", "LIB_PATH"]

@@ -8,7 +8,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libmlaq.so")
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("api.cpp", "decode.hip", "quant.hip", "extend.hip", "extend_attn.hip")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("api.cpp", "decode.hip", "quant.hip", "extend.hip", "extend_attn.hip", "probe.hip")]
 HEADERS = [os.path.join(HERE, "csrc", f) for f in ("device_common.h", "mlaq_kernels.h")] + \
     [os.path.join(ROOT, "include", "mlaq.h")]
 

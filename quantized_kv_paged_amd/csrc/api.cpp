@@ -499,4 +499,15 @@ mlaq_status kv_dequantize(mlaq_format src_format, const uint8_t* kv_data, const 
   return MLAQ_OK;
 }
 
+mlaq_status mlaq_read_probe(const void* buf, int64_t bytes, void* partials, int32_t num_blocks, hipStream_t stream) {
+  if (bytes < 0 || bytes % 16) return fail(MLAQ_ERR_SHAPE, "read probe: bytes %lld must be a multiple of 16", (long long)bytes);
+  if (num_blocks < 1 || num_blocks > (1 << 20))
+    return fail(MLAQ_ERR_SHAPE, "read probe: num_blocks %d not in [1, 2^20]", num_blocks);
+  if (!partials || (bytes > 0 && !buf)) return fail(MLAQ_ERR_NULL, "read probe: a required pointer is NULL");
+  if (!aligned(buf, 16) || !aligned(partials, 16)) return fail(MLAQ_ERR_ALIGN, "read probe: buf and partials need 16-byte alignment");
+  hipError_t e = mlaq::launch_read_probe(buf, bytes / 16, partials, num_blocks, stream);
+  if (e != hipSuccess) return fail(MLAQ_ERR_LAUNCH, "read probe launch failed: %s", hipGetErrorString(e));
+  return MLAQ_OK;
+}
+
 }  // extern "C"

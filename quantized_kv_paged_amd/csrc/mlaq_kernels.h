@@ -115,5 +115,7 @@ int extend_attn_tile_rows();
 int extend_attn_tokens_per_group();
 // the merge pass of the decode kernels on its own (partials already written)
 hipError_t launch_merge(const DecodeArgs& a, hipStream_t stream);
+// streaming-read probe: `words` 16-byte words of buf, one 16-byte XOR per block to partials
+hipError_t launch_read_probe(const void* buf, int64_t words, void* partials, int blocks, hipStream_t stream);
 
 }  // namespace mlaq

@@ -111,6 +111,16 @@ def test_quantize_and_dequantize_validation():
     assert e.value.status == ERR_SHAPE and "num_rows" in str(e.value)
 
 
+def test_read_probe_validation():
+    L = qk._lib
+    assert L.mlaq_read_probe(FAKE, 24, FAKE, 8, None) == ERR_SHAPE      # not whole 16-byte words
+    assert L.mlaq_read_probe(FAKE, -16, FAKE, 8, None) == ERR_SHAPE
+    assert L.mlaq_read_probe(FAKE, 64, FAKE, 0, None) == ERR_SHAPE
+    assert L.mlaq_read_probe(None, 64, FAKE, 8, None) == ERR_NULL
+    assert L.mlaq_read_probe(FAKE, 64, None, 8, None) == ERR_NULL
+    assert L.mlaq_read_probe(FAKE + 8, 64, FAKE, 8, None) == ERR_ALIGN
+
+
 def test_split_planning_and_workspace():
     import synth
     # (FP8 plan, NVFP4 plan): FP8 workgroups stream 64-token tiles, two per CU; NVFP4
