@@ -9,13 +9,14 @@
 // (aitop.news, implementation item 3) describes for decode: packed tiles and E4M3 block
 // scales read as stored, converted in registers, global scale applied as a scalar factor.
 //
-// gfx950 design: one workgroup of 4 waves = one request x one KV chunk x 16 heads; two
-// workgroups share a CU (80 KB of LDS and at most 256 VGPRs each), so every SIMD runs two
-// waves of independent workgroups.
+// gfx950 design: one workgroup = one request x one KV chunk x 16 heads, running NS
+// online-softmax streams (token groups) with two waves each.  FP8 and BF16: NS = 2, 4 waves,
+// 80 KB of LDS, two workgroups per CU; NVFP4: NS = 1, 2 waves, 40 KB, four per CU.  Either
+// way every SIMD runs two waves (at most 256 VGPRs each) of independent workgroups.
 //   * every head shares the single latent KV row, so each KV byte is read from HBM once and
 //     both products are dense 16-head contractions on MFMA;
-//   * tile = 64 tokens.  Wave w = (token group tg = w % 2, dim half dh = w / 2) owns tokens
-//     32tg .. 32tg+31 of each tile as two 16-token MFMA blocks.  S^T = K Q^T
+//   * tile = 32 NS tokens.  Wave w = (token group tg = w % NS, dim half dh = w / NS) owns
+//     tokens 32tg .. 32tg+31 of each tile as two 16-token MFMA blocks.  S^T = K Q^T
 //     (v_mfma_f32_16x16x32) is split over the pair (tg, 0) / (tg, 1): half dh is value dims
 //     256dh .. 256dh+255 plus rope dims 512+32dh .. +31; each wave holds that half of the query
 //     operand and converts that half of its 32 rows, and the pair swaps 2 KB of partial scores
@@ -24,10 +25,10 @@
 //     per head are already in the A-operand layout of a 32-token v_mfma_f32_16x16x32 (lane =
 //     head, 8 tokens), so O += P V needs no score traffic: wave (tg, dh) accumulates the 256
 //     value dims of half dh over its 32 tokens, the V operand coming from LDS with two gfx950
-//     transposed reads (ds_read_b64_tr_b16) per 16 dims.  The two streams are merged in LDS at
-//     the end of the chunk;
-//   * K rows go global -> VGPR: for pages of at least 64 tokens a tile is 64 contiguous pool
-//     rows, read with buffer loads through a per-tile descriptor whose size admits only the
+//     transposed reads (ds_read_b64_tr_b16) per 16 dims.  At the end of the chunk the streams
+//     are merged through the waves' own value tiles (one barrier);
+//   * K rows go global -> VGPR: with pages of at least a tile, a tile is contiguous pool rows,
+//     read with buffer loads through a per-tile descriptor whose size admits only the
 //     tile's valid rows (other lanes read zeros); the registers of a tile are refilled with
 //     the next tile's loads as soon as they are converted, so the loads are in flight during
 //     the softmax and PV of the tile.  Rows are converted to fp16 in registers (FP8: exact;
