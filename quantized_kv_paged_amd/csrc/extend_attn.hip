@@ -37,7 +37,11 @@ __device__ __forceinline__ int xoff(int r, int c) { return r * kXRowB + 16 * ((c
 
 __global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kXSmem];
-  const int blk = blockIdx.x, b = blockIdx.y, split = blockIdx.z;
+  // workgroups in dispatch order take the requests' token blocks from the last (the most rows
+  // in a causal chunk) to the first, all requests at each step, so the longest work starts
+  // first and the short blocks fill in behind it
+  const int lin = blockIdx.x + gridDim.x * blockIdx.y;
+  const int b = lin % gridDim.y, blk = gridDim.x - 1 - lin / gridDim.y, split = blockIdx.z;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
   const int pi = w >> 1, dh = w & 1;             // token of the pair, dim half
 
