@@ -3,7 +3,8 @@
  * A small C ABI.  Pointers are DEVICE pointers unless marked (host).  The caller owns
  * all memory: queries, pools, page table, lengths, outputs and the workspace.  Calls
  * are asynchronous on `stream`; they never allocate, never synchronise the device and
- * never read device memory on the host.  Every argument that can be checked on the
+ * never read device memory on the host, so a call can be captured in a HIP graph and
+ * replayed (its launches use no memset or copy nodes).  Every argument that can be checked on the
  * host is checked before any launch; a non-OK status means nothing was launched and
  * mlaq_last_error() (thread-local) says why.
  *
