@@ -139,6 +139,36 @@ def read_probe(qk, torch, split_gbs, reps=10):
             "split_kernel_frac_of_probe": round(split_gbs / gbs, 4)}
 
 
+def graph_steps(make_step, n_layers, steps, torch, kv_bytes):
+    """The same steps replayed from a HIP graph: one graph holds one step per pool copy, captured
+    on a side stream, and is replayed until about `steps` steps have run; gives ms per step
+    without per-launch host work."""
+    gs = torch.cuda.Stream()
+    gstep = make_step(gs.cuda_stream)
+    with torch.cuda.stream(gs):
+        for l in range(n_layers):
+            gstep(l)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=gs):
+        for l in range(n_layers):
+            gstep(l)
+    reps = max(1, steps // n_layers)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(gs):
+        start.record()
+        for _ in range(reps):
+            g.replay()
+        end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / (reps * n_layers)
+    return {"ms_per_step": round(ms, 5), "steps": reps * n_layers,
+            "kv_gbs": round(kv_bytes / (ms * 1e-3) / 1e9, 1)}
+
+
 def pmc_traffic(kernel_tag: str, launches_bytes: float):
     """HBM bytes per launch from committed rocprofv3 counter summaries, if they were taken on
     the current kernel source; else None."""
@@ -234,7 +264,7 @@ def main():
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -270,23 +300,30 @@ def main():
         if st != 0:
             raise RuntimeError(qk.last_error())
 
+    def make_step(strm):
+        """One step (layer l) launched on the HIP stream handle strm."""
+        com = common[:-1] + (strm,)
+        if fmt == "fp8":
+            fp8p = [t.data_ptr() for t in d["fp8"]]
+            return lambda l: check(L.mla_decode_fp8(pp, qp, fp8p[l], 1.0, *com))
+        nvp = [(a.data_ptr(), s.data_ptr()) for a, s in d["nv"]]
+        if w.write_tokens:
+            def wstep(l):
+                check(L.kv_quantize_nvfp4(wsrc.data_ptr(), qk.MLAQ_FP8_E4M3, 1.0, w.write_tokens,
+                                          wslots.data_ptr(), nvp[l][0], nvp[l][1], w.pool_tokens, 1.0, strm))
+                check(L.mla_decode_nvfp4(pp, qp, nvp[l][0], nvp[l][1], 1.0, *com))
+            return wstep
+        return lambda l: check(L.mla_decode_nvfp4(pp, qp, nvp[l][0], nvp[l][1], 1.0, *com))
+
     if fmt == "fp8":
-        fp8p = [t.data_ptr() for t in d["fp8"]]
-        step = lambda l: check(L.mla_decode_fp8(pp, qp, fp8p[l], 1.0, *common))
         kv_bytes = w.batch * w.kv_len * FP8_ROW
     else:
         nvp = [(a.data_ptr(), s.data_ptr()) for a, s in d["nv"]]
         if w.write_tokens:
             wsrc = torch.from_numpy(synth.write_source_fp8(w)).cuda()
             wslots = torch.from_numpy(synth.slot_mapping(w, pt)).cuda()
-
-            def step(l):
-                check(L.kv_quantize_nvfp4(wsrc.data_ptr(), qk.MLAQ_FP8_E4M3, 1.0, w.write_tokens,
-                                          wslots.data_ptr(), nvp[l][0], nvp[l][1], w.pool_tokens, 1.0, stream))
-                check(L.mla_decode_nvfp4(pp, qp, nvp[l][0], nvp[l][1], 1.0, *common))
-        else:
-            step = lambda l: check(L.mla_decode_nvfp4(pp, qp, nvp[l][0], nvp[l][1], 1.0, *common))
         kv_bytes = w.batch * w.kv_len * NV_ROW
+    step = make_step(stream)
 
     ms, split_ms, merge_ms, ms_ev = timed_steps(step, n_layers, args.steps, args.warmup, hip, torch)
     achieved = kv_bytes / (split_ms * 1e-3) / 1e9
@@ -314,6 +351,7 @@ def main():
 
     if not args.no_extras:
         res["read_probe"] = read_probe(qk, torch, achieved)
+        res["graph"] = graph_steps(make_step, n_layers, args.steps, torch, kv_bytes)
 
     if args.copy_calibration:
         # a plain copy kernel of known size: its FETCH_SIZE / WRITE_SIZE per dispatch give the
