@@ -139,8 +139,9 @@ mlaq_status mla_decode_nvfp4_append(const mlaq_decode_params* p, const uint16_t*
  * (e4m3 of fl32(e2m1 * e4m3 * global_scale) / chunk_scale: lossy, up to 6 significant bits
  * round to 4), the chunk's FP8 rows are appended, attention runs over that workspace, and
  * the chunk is then quantized into the cache at slot_mapping[t] (kv_quantize_nvfp4 with
- * src_scale = chunk_scale; rows < 0 skipped).  Attention uses the FP8 decode kernels, one
- * query token (all its heads) per workspace view.
+ * src_scale = chunk_scale; rows < 0 skipped).  The attention reads each workspace row once
+ * per four chunk tokens and 16-head group, on MFMA; KV splits of long prefixes are merged
+ * like the decode splits.
  *   q          bf16 [num_q, num_heads, 576]      chunk_kv  e4m3fn [num_q, 576], x = e4m3 * chunk_scale
  *   qo_indptr  int32 [batch + 1]                  prefix_lens int32 [batch]
  *   out        fp32 [num_q, num_heads, 512]       lse fp32 [num_q, num_heads] or NULL
@@ -148,8 +149,8 @@ mlaq_status mla_decode_nvfp4_append(const mlaq_decode_params* p, const uint16_t*
  * outside [0, max_*_len], whose pages do not cover its prefix or whose query range leaves
  * [0, num_q) gets NaN; a prefix page outside the pool gives NaN for the tokens that see it.
  * The workspace (mlaq_extend_workspace_bytes(p), 256-B aligned) holds batch regions of
- * round_up(max_prefix_len + max_chunk_len, 64) FP8 rows, the per-token views and the
- * decode partials; it is reused across layers. */
+ * round_up(max_prefix_len + max_chunk_len, 64) FP8 rows, per-token lengths and the split
+ * partials; it is reused across layers. */
 typedef struct {              /* (host) */
   int32_t batch;              /* requests, 0 .. 65535 */
   int32_t num_heads;          /* multiple of 16, 16 .. 128 */

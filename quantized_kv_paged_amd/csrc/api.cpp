@@ -167,13 +167,13 @@ mlaq_status decode_common(int fmt, const mlaq_decode_params* p, const uint16_t* 
   return MLAQ_OK;
 }
 
-// Extend: workspace layout (FP8 regions, per-token views, decode partials), each part
-// 256-byte aligned, and the decode parameters of the per-token views.
+// Extend: workspace layout (FP8 regions, per-token lengths and page ranges, split partials),
+// each part 256-byte aligned, the KV splits of the attention, and the decode parameters the
+// merge kernel's bounds check reads (one "request" per chunk token).
 struct ExtendLayout {
   int region_rows = 0, npp = 0;
-  bool tiled = false;             // 16 heads: shared-tile extend attention; otherwise decode views
   int tsplits = 1, tiles_per_split = 1;
-  size_t rows_off = 0, idx_off = 0, lens_off = 0, indptr_off = 0, part_off = 0, part_bytes = 0, total = 0;
+  size_t rows_off = 0, lens_off = 0, indptr_off = 0, part_off = 0, part_bytes = 0, total = 0;
   mlaq_decode_params dp{};
 };
 
@@ -191,7 +191,7 @@ mlaq_status extend_layout(const mlaq_extend_params* p, ExtendLayout& L) {
   const int64_t span = (int64_t)p->max_prefix_len + p->max_chunk_len;
   L.region_rows = (int)((span + mlaq::kExtendPage - 1) / mlaq::kExtendPage * mlaq::kExtendPage);
   L.npp = L.region_rows / mlaq::kExtendPage;
-  // the per-token views are int32 page tables over batch regions of npp pages
+  // the per-token page ranges are int32 offsets t * npp
   if ((int64_t)p->num_q * L.npp >= ((int64_t)1 << 31) || (int64_t)p->batch * L.npp >= ((int64_t)1 << 31))
     return fail(MLAQ_ERR_SHAPE, "extend views too large: num_q %d / batch %d x %d pages per region", p->num_q,
                 p->batch, L.npp);
@@ -209,26 +209,23 @@ mlaq_status extend_layout(const mlaq_extend_params* p, ExtendLayout& L) {
   if (p->pool_tokens <= 0 || p->pool_tokens > ((int64_t)1 << 40))
     return fail(MLAQ_ERR_SHAPE, "pool_tokens %lld out of range", (long long)p->pool_tokens);
   L.rows_off = 0;
-  L.idx_off = align256((size_t)p->batch * L.region_rows * 576);
-  L.lens_off = L.idx_off + align256((size_t)p->num_q * L.npp * 4);
+  L.lens_off = align256((size_t)p->batch * L.region_rows * 576);
   L.indptr_off = L.lens_off + align256((size_t)p->num_q * 4);
   L.part_off = L.indptr_off + align256((size_t)(p->num_q + 1) * 4);
-  L.tiled = p->num_heads == 16;
-  if (L.tiled) {
-    // KV splits so that the workgroups (one per kXT chunk tokens of a request, one per CU)
-    // cover the CUs at least once; each split takes a whole number of 32-row tiles
+  {
+    // KV splits so that the workgroups (one per kXT chunk tokens of a request and 16-head
+    // group, one per CU) cover the CUs at least once; each split takes whole 32-row tiles
     const int tile = mlaq::extend_attn_tile_rows(), per_group = mlaq::extend_attn_tokens_per_group();
     const int max_tiles = (int)((span + tile - 1) / tile);
-    const int64_t groups = (int64_t)p->batch * ((p->max_chunk_len + per_group - 1) / per_group);
+    const int64_t groups = (int64_t)p->batch * ((p->max_chunk_len + per_group - 1) / per_group) * (p->num_heads / 16);
     int s_ = p->num_splits > 0 ? p->num_splits
                                : (int)std::min<int64_t>(MLAQ_MAX_SPLITS, groups > 0 ? (mlaq::kComputeUnits + groups - 1) / groups : 1);
     s_ = std::max(1, std::min(s_, std::max(1, max_tiles)));
     L.tiles_per_split = std::max(1, (max_tiles + s_ - 1) / s_);
     L.tsplits = (max_tiles + L.tiles_per_split - 1) / L.tiles_per_split;
     if (L.tsplits < 1) L.tsplits = 1;
-    L.part_bytes = L.tsplits > 1 ? align256((size_t)p->num_q * L.tsplits * (16 * 512 * 4 + 32 * 4)) : 0;
-  } else {
-    L.part_bytes = workspace_for(&L.dp, resolve_splits(mlaq::FMT_FP8, &L.dp));
+    L.part_bytes = L.tsplits > 1 ? align256((size_t)p->num_q * L.tsplits * (p->num_heads / 16) * (16 * 512 * 4 + 32 * 4))
+                                 : 0;
   }
   L.total = L.part_off + L.part_bytes;
   return MLAQ_OK;
@@ -318,7 +315,7 @@ size_t mlaq_extend_workspace_bytes(const mlaq_extend_params* p) {
 int32_t mlaq_extend_num_splits(const mlaq_extend_params* p) {
   ExtendLayout L;
   if (extend_layout(p, L) != MLAQ_OK) return 0;
-  return L.tiled ? L.tsplits : resolve_splits(mlaq::FMT_FP8, &L.dp);
+  return L.tsplits;
 }
 
 mlaq_status mla_extend_nvfp4(const mlaq_extend_params* p, const uint16_t* q, const int32_t* qo_indptr,
@@ -354,7 +351,6 @@ mlaq_status mla_extend_nvfp4(const mlaq_extend_params* p, const uint16_t* q, con
   a.kv_scales = kv_scales;
   a.chunk_kv = chunk_kv;
   a.ws_rows = ws + L.rows_off;
-  a.view_indices = reinterpret_cast<int32_t*>(ws + L.idx_off);
   a.view_lens = reinterpret_cast<int32_t*>(ws + L.lens_off);
   a.view_indptr = reinterpret_cast<int32_t*>(ws + L.indptr_off);
   a.pool_tokens = p->pool_tokens;
@@ -367,12 +363,12 @@ mlaq_status mla_extend_nvfp4(const mlaq_extend_params* p, const uint16_t* q, con
   a.region_rows = L.region_rows;
   a.global_scale = global_scale;
   a.chunk_scale = chunk_scale;
-  a.write_pages = L.tiled ? 0 : 1;
-  a.nan_out = L.tiled && L.tsplits == 1 ? out : nullptr;
-  a.nan_lse = L.tiled && L.tsplits == 1 ? lse : nullptr;
+  a.num_heads = p->num_heads;
+  a.nan_out = L.tsplits == 1 ? out : nullptr;
+  a.nan_lse = L.tsplits == 1 ? lse : nullptr;
   hipError_t e = mlaq::launch_extend_views(a, stream);
   if (e != hipSuccess) return fail(MLAQ_ERR_LAUNCH, "extend view launch failed: %s", hipGetErrorString(e));
-  if (L.tiled) {
+  {
     mlaq::ExtendAttnArgs x;
     x.q = q;
     x.ws_rows = a.ws_rows;
@@ -382,9 +378,10 @@ mlaq_status mla_extend_nvfp4(const mlaq_extend_params* p, const uint16_t* q, con
     x.out = out;
     x.lse = lse;
     x.part_o = L.part_bytes ? reinterpret_cast<float*>(ws + L.part_off) : nullptr;
-    x.part_ml = L.part_bytes ? x.part_o + (size_t)p->num_q * L.tsplits * 16 * 512 : nullptr;
+    x.part_ml = L.part_bytes ? x.part_o + (size_t)p->num_q * L.tsplits * (p->num_heads / 16) * 16 * 512 : nullptr;
     x.batch = p->batch;
     x.num_q = p->num_q;
+    x.num_heads = p->num_heads;
     x.page_size = p->page_size;
     x.max_prefix_len = p->max_prefix_len;
     x.max_chunk_len = p->max_chunk_len;
@@ -408,7 +405,7 @@ mlaq_status mla_extend_nvfp4(const mlaq_extend_params* p, const uint16_t* q, con
       m.part_o = x.part_o;
       m.part_ml = x.part_ml;
       m.batch = p->num_q;
-      m.num_heads = 16;
+      m.num_heads = p->num_heads;
       m.page_size = mlaq::kExtendPage;
       m.max_kv_len = L.dp.max_kv_len;
       m.num_splits = L.tsplits;
@@ -419,10 +416,6 @@ mlaq_status mla_extend_nvfp4(const mlaq_extend_params* p, const uint16_t* q, con
       if (ev.merge_end) (void)hipEventRecord(ev.merge_end, stream);
       if (e != hipSuccess) return fail(MLAQ_ERR_LAUNCH, "extend merge launch failed: %s", hipGetErrorString(e));
     }
-  } else {
-    st = decode_common(mlaq::FMT_FP8, &L.dp, q, a.ws_rows, nullptr, chunk_scale, a.view_indptr, a.view_indices,
-                       a.view_lens, out, lse, L.part_bytes ? ws + L.part_off : nullptr, L.part_bytes, stream);
-    if (st != MLAQ_OK) return st;
   }
   return kv_quantize_nvfp4(chunk_kv, MLAQ_FP8_E4M3, chunk_scale, p->num_q, slot_mapping, kv_data, kv_scales,
                            p->pool_tokens, global_scale, stream);

@@ -8,11 +8,12 @@
 //     0 .. P-1 are the prefix (pool rows through the page table, value
 //     e4m3(fl32(fl32(fl32(e2m1 * e4m3) * g) / chunk_scale))), rows P .. P+C-1 are the chunk's
 //     FP8 rows copied as they are, so every workspace byte is in the chunk's scale domain;
-//   - extend_index_kernel gives chunk token i of the request a causal view of its region:
-//     a page list over the region and a length of P + i + 1 rows (the token sees the prefix,
-//     the chunk tokens before it and itself);
-//   - the FP8 decode kernels then attend every chunk token over its view (one query token
-//     with its heads per decode "request"), and kv_quantize_nvfp4 writes the chunk.
+//   - extend_index_kernel gives chunk token i of the request its causal length, P + i + 1
+//     rows of the region (the token sees the prefix, the chunk tokens before it and itself),
+//     and a range of region pages in a per-token numbering that the merge kernel's bounds
+//     check reads; tokens of invalid requests get NaN outputs here;
+//   - extend_attn_kernel attends the chunk tokens over their rows, and kv_quantize_nvfp4
+//     writes the chunk.
 // Requests whose lengths or pages are out of range get a length of -1 (NaN outputs) and no
 // workspace rows; a prefix page outside the pool gives NaN codes in its rows.
 #pragma clang fp contract(off)
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(256) void extend_gather_kernel(ExtendArgs a) {
 }
 
 // one workgroup of 64 threads per query token t (grid num_q): its request (binary search in
-// qo_indptr), its length P + i + 1 and its page list (region pages of the request, 64 rows each)
+// qo_indptr), its length P + i + 1 and its page range (region_rows / 64 pages from t * that)
 __global__ __launch_bounds__(64) void extend_index_kernel(ExtendArgs a) {
   const int t = blockIdx.x, lane = threadIdx.x;
   const int npp = a.region_rows / kExtendPage;
@@ -107,12 +108,12 @@ __global__ __launch_bounds__(64) void extend_index_kernel(ExtendArgs a) {
   int P, C, q0;
   const bool ok = extend_bounds(a, b, P, C, q0) && t >= q0 && t < q0 + C;
   if (lane == 0) a.view_lens[t] = ok ? P + (t - q0) + 1 : -1;
-  if (a.write_pages)
-    for (int k = lane; k < npp; k += 64) a.view_indices[(int64_t)t * npp + k] = b * npp + k;
-  if (!ok && a.nan_out) {   // the tiled attention skips invalid requests: their outputs are NaN
-    float* o = a.nan_out + (int64_t)t * 16 * kDV;
-    for (int k = lane; k < 16 * kDV; k += 64) o[k] = NAN;
-    if (a.nan_lse && lane < 16) a.nan_lse[(int64_t)t * 16 + lane] = NAN;
+  if (!ok && a.nan_out) {   // the attention skips invalid requests: their outputs are NaN
+    const int H = a.num_heads;
+    float* o = a.nan_out + (int64_t)t * H * kDV;
+    for (int k = lane; k < H * kDV; k += 64) o[k] = NAN;
+    if (a.nan_lse)
+      for (int k = lane; k < H; k += 64) a.nan_lse[(int64_t)t * H + k] = NAN;
   }
 }
 

@@ -43,7 +43,9 @@ __global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArg
   // in a causal chunk) to the first, all requests at each step, so the longest work starts
   // first and the short blocks fill in behind it
   const int lin = blockIdx.x + gridDim.x * blockIdx.y;
-  const int b = lin % gridDim.y, blk = gridDim.x - 1 - lin / gridDim.y, split = blockIdx.z;
+  const int b = lin % gridDim.y, blk = gridDim.x - 1 - lin / gridDim.y;
+  const int H = a.num_heads, HG = H >> 4;        // 16-head groups, each its own workgroups
+  const int split = blockIdx.z / HG, hg = blockIdx.z - split * HG;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
   const int pi = w >> 1, dh = w & 1;             // token of the pair, dim half
 
@@ -111,7 +113,7 @@ __global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArg
   f16x8 qop[9];
   float score_scale;
   {
-    const uint16_t* qrow = a.q + ((int64_t)t * 16 + l16) * kD;
+    const uint16_t* qrow = a.q + ((int64_t)t * H + 16 * hg + l16) * kD;
     u32x4 qraw[9];
 #pragma unroll
     for (int kb = 0; kb < 9; ++kb) qraw[kb] = *reinterpret_cast<const u32x4*>(qrow + xdim(kb));
@@ -243,15 +245,15 @@ __global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArg
       const float L = __shfl(l_run, h);
       float f = L > 0.0f ? a.out_scale / L : 0.0f;
       if (L != L) f = L;
-      float* dst = a.out + ((int64_t)t * 16 + h) * kDV + 256 * dh + l16;
+      float* dst = a.out + ((int64_t)t * H + 16 * hg + h) * kDV + 256 * dh + l16;
 #pragma unroll
       for (int nt = 0; nt < 16; ++nt) dst[16 * nt] = o[nt][i] * f;
     }
     if (a.lse && dh == 0 && grp == 0)
-      a.lse[(int64_t)t * 16 + l16] = l_run > 0.0f ? (m_run + __log2f(l_run)) * kLn2
+      a.lse[(int64_t)t * H + 16 * hg + l16] = l_run > 0.0f ? (m_run + __log2f(l_run)) * kLn2
                                                    : (l_run != l_run ? l_run : -INFINITY);
   } else {
-    const int64_t slot = (int64_t)t * a.num_splits + split;
+    const int64_t slot = ((int64_t)t * a.num_splits + split) * HG + hg;   // the decode partial layout
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float* dst = a.part_o + slot * (16 * kDV) + (4 * grp + i) * kDV + 256 * dh + l16;
@@ -267,7 +269,7 @@ __global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArg
 
 hipError_t launch_extend_attn(const ExtendAttnArgs& a, hipStream_t stream) {
   const int nblk = (a.max_chunk_len + kXT - 1) / kXT;
-  hipLaunchKernelGGL(extend_attn_kernel, dim3((unsigned)nblk, (unsigned)a.batch, (unsigned)a.num_splits),
+  hipLaunchKernelGGL(extend_attn_kernel, dim3((unsigned)nblk, (unsigned)a.batch, (unsigned)(a.num_splits * (a.num_heads / 16))),
                      dim3(kXThreads), 0, stream, a);
   return hipGetLastError();
 }

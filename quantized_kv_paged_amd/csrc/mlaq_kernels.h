@@ -84,30 +84,29 @@ struct ExtendArgs {
   const uint8_t* kv_scales;
   const uint8_t* chunk_kv;    // e4m3fn [num_q, 576]
   uint8_t* ws_rows;           // e4m3fn [B, region_rows, 576]
-  int32_t* view_indptr;       // [num_q + 1]
-  int32_t* view_indices;      // [num_q, region_rows / kExtendPage]
-  int32_t* view_lens;         // [num_q]
-  float* nan_out;             // with the tiled attention: outputs of invalid tokens set to NaN here
-  float* nan_lse;
-  int32_t write_pages;        // 0: view_indices not needed (tiled attention)
+  int32_t* view_indptr;       // [num_q + 1] token t: rows t * region pages (bounds for the merge)
+  int32_t* view_lens;         // [num_q] rows token t sees, or -1
+  float* nan_out;             // outputs [num_q, num_heads, 512] of invalid tokens set to NaN here
+  float* nan_lse;             // (one split; with several the merge writes them)
   int64_t pool_tokens;
-  int32_t batch, num_q, page_size, page_shift, max_prefix_len, max_chunk_len, region_rows;
+  int32_t batch, num_q, num_heads, page_size, page_shift, max_prefix_len, max_chunk_len, region_rows;
   float global_scale, chunk_scale;
 };
 hipError_t launch_extend_views(const ExtendArgs& a, hipStream_t stream);
 
-// Extend attention with one shared K/V tile per workgroup of kXT chunk tokens (16 heads).
+// Extend attention with one shared K/V tile per workgroup of kXT chunk tokens and 16 heads.
 struct ExtendAttnArgs {
-  const uint16_t* q;          // bf16 [num_q, 16, 576]
+  const uint16_t* q;          // bf16 [num_q, num_heads, 576]
   const uint8_t* ws_rows;     // e4m3fn [batch, region_rows, 576]
   const int32_t* qo_indptr;
   const int32_t* prefix_lens;
   const int32_t* kv_indptr;   // cache page table (bounds check of the prefix only)
-  float* out;                 // [num_q, 16, 512] (one split)
+  float* out;                 // [num_q, num_heads, 512] (one split)
   float* lse;
-  float* part_o;              // [num_q, num_splits, 16, 512] (several splits)
-  float* part_ml;             // [num_q, num_splits, 32]
-  int32_t batch, num_q, page_size, max_prefix_len, max_chunk_len, region_rows, num_splits, tiles_per_split;
+  float* part_o;              // [num_q, num_splits, num_heads / 16, 16, 512] (several splits)
+  float* part_ml;             // [num_q, num_splits, num_heads / 16, 32]
+  int32_t batch, num_q, num_heads, page_size, max_prefix_len, max_chunk_len, region_rows, num_splits,
+      tiles_per_split;
   float score_scale, out_scale;
 };
 hipError_t launch_extend_attn(const ExtendAttnArgs& a, hipStream_t stream);

@@ -218,11 +218,15 @@ def test_extend_validation_and_workspace():
     assert _ext(p, ws=FAKE + 16) == ERR_ALIGN
     assert _ext(_ext_p(num_q=0), q=None, qo=None, ckv=None) == 0    # nothing to do
     # workspace: one FP8 region of round_up(prefix + chunk, 64) rows per request, the per-token
-    # views, then the partials of the KV splits (16 heads: the shared-tile kernel's splits)
+    # lengths and page offsets, then the partials of the KV splits per 16-head group
     region = -(-(4096 + 32) // 64) * 64
-    s = qk._lib.mlaq_extend_num_splits(ctypes.byref(p))
-    assert s >= 1
     a256 = lambda x: -(-x // 256) * 256
-    base = a256(2 * region * 576) + a256(64 * (region // 64) * 4) + a256(64 * 4) + a256(65 * 4)
-    assert need == base + (a256(64 * s * (16 * 512 * 4 + 32 * 4)) if s > 1 else 0)
+    base = a256(2 * region * 576) + a256(64 * 4) + a256(65 * 4)
+    for heads in (16, 64):
+        ph = _ext_p(num_heads=heads)
+        s = qk._lib.mlaq_extend_num_splits(ctypes.byref(ph))
+        assert s >= 1
+        assert qk.mlaq_extend_workspace_bytes(ph) == base + (
+            a256(64 * s * (heads // 16) * (16 * 512 * 4 + 32 * 4)) if s > 1 else 0)
+    assert need == qk.mlaq_extend_workspace_bytes(_ext_p(num_heads=16))
     assert qk._lib.mlaq_extend_workspace_bytes(ctypes.byref(_ext_p(num_heads=20))) == ctypes.c_size_t(-1).value

@@ -85,6 +85,23 @@ def test_extend_32_heads():
     _run([300], [20], 64, seed=53, heads=32)
 
 
+def test_extend_128_heads_and_splits():
+    """Eight 16-head groups, each its own workgroups over the shared rows; one and several KV
+    splits (the merge kernel then reads the per-group partials)."""
+    _run([190, 0], [9, 6], 64, seed=56, splits=(0, 1, 3), heads=128)
+
+
+def test_bad_prefix_nan_with_64_heads():
+    """Tokens of an invalid request get NaN in every head group, with one split (the view builder
+    writes them) and with several (the merge kernel does)."""
+    prefix, chunk = [30, 70], [5, 2]
+    bad = np.asarray([30, -3], np.int32)
+    for s in (1, 2):
+        out, lse, out_ref, lse_ref, qo = _run(prefix, chunk, 64, seed=57, splits=(s,), heads=64, prefix_lens_dev=bad)
+        assert np.isnan(out[qo[1]:qo[2]]).all() and np.isnan(lse[qo[1]:qo[2]]).all()
+        assert_parity(out[:qo[1]], lse[:qo[1]], out_ref[:qo[1]], lse_ref[:qo[1]], tag=f"64 heads splits={s}")
+
+
 def test_extend_bad_prefix_length_gives_nan_for_its_tokens():
     prefix, chunk = [50, 80], [4, 3]
     bad = np.asarray([50, 10 ** 6], np.int32)                 # above max_prefix_len
