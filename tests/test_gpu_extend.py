@@ -81,6 +81,12 @@ def test_extend_scales(g, cs):
     _run([129, 40], [17, 1], 16, seed=52, splits=(0, 2), g=g, chunk_scale=cs)
 
 
+def test_extend_request_with_empty_chunk():
+    """A request with no chunk tokens (prefix only) between two that have some: it owns no
+    query rows, and the others' results and cache writes are unaffected."""
+    _run([100, 50, 0], [3, 0, 7], 64, seed=58, splits=(0, 2))
+
+
 def test_extend_32_heads():
     _run([300], [20], 64, seed=53, heads=32)
 
