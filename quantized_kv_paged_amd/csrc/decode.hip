@@ -726,8 +726,8 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
 // w_s = 2^(m_s - M) over the splits (M = max_s m_s), output = sum_s w_s O_s / sum_s w_s l_s,
 // natural-log lse.  The 256 threads are 1024 / DIMS groups of DIMS / 4 lanes; group k sums the
 // splits s = k (mod groups), each lane 4 dims, so every load of a group is DIMS x 4 contiguous
-// bytes.  Narrow chunks (DIMS = 64 or 128) spread small batches over many workgroups; wide
-// ones (DIMS = 256) keep large batches from repeating the weight computation.  Every load that
+// bytes.  Narrow chunks (DIMS = 32, 64 or 128) spread small batches over many workgroups;
+// wide ones (DIMS = 256) keep large batches from repeating the weight computation.  Every load that
 // does not depend on another one (the first batch of partials, all (m, l) pairs, the request's
 // bounds) is issued up front, so the kernel pays one memory latency before its reductions;
 // later batches of partials are loaded one batch ahead of their use.
@@ -841,12 +841,16 @@ static hipError_t launch(K kernel, dim3 grid, dim3 block, hipStream_t stream, hi
 
 // Merge shape: small batches spread over more workgroups (narrow dim chunks); with at most
 // 64 splits, 128-dim chunks (two batches of loads, half the workgroups) measured faster than
-// 64-dim ones (5.2 vs 5.5 us at 8 requests x 16 heads x 64 splits), with more splits slower
+// 64-dim ones (5.2 vs 5.5 us at 8 requests x 16 heads x 64 splits), with more splits slower;
+// with hundreds of splits, 32-dim chunks (twice the lane groups, half the batches per
+// workgroup) were faster again (7.7 vs 8.2 us at 2 requests x 512 splits)
 static hipError_t launch_fmt_merge(const DecodeArgs& a, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
   if (a.batch * a.num_heads <= 256) {
     if (a.part_splits <= 64)
       return launch(mla_merge_kernel<128>, dim3(kDV / 128, a.num_heads, a.batch), dim3(kMergeThreads), stream, t0,
                     t1, a);
+    if (a.part_splits > 256)
+      return launch(mla_merge_kernel<32>, dim3(kDV / 32, a.num_heads, a.batch), dim3(kMergeThreads), stream, t0, t1, a);
     return launch(mla_merge_kernel<64>, dim3(kDV / 64, a.num_heads, a.batch), dim3(kMergeThreads), stream, t0, t1, a);
   }
   return launch(mla_merge_kernel<256>, dim3(kDV / 256, a.num_heads, a.batch), dim3(kMergeThreads), stream, t0, t1,
