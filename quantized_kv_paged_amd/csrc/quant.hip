@@ -23,11 +23,11 @@ __global__ __launch_bounds__(256) void nvfp4_quantize_kernel(QuantArgs a) {
   if (gid >= a.num_tokens * 36) return;
   const int64_t t = gid / 36;
   const int k = (int)(gid - t * 36);
+  // the slot and the source block are loaded together; the slot is checked afterwards
   const int64_t slot = a.slots[t];
-  if (slot < 0 || slot >= a.pool_tokens) return;
-
   float x[16];
   load_src_block(reinterpret_cast<const uint8_t*>(a.src) + t * kD * (a.src_bf16 ? 2 : 1), a.src_bf16, a.src_scale, k, x);
+  if (slot < 0 || slot >= a.pool_tokens) return;
   u32x2 packed;
   uint32_t sb;
   nvfp4_quantize_block(x, a.global_scale, packed, sb);
