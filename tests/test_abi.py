@@ -5,6 +5,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -230,3 +231,21 @@ def test_extend_validation_and_workspace():
             a256(64 * s * (heads // 16) * (16 * 512 * 4 + 32 * 4)) if s > 1 else 0)
     assert need == qk.mlaq_extend_workspace_bytes(_ext_p(num_heads=16))
     assert qk._lib.mlaq_extend_workspace_bytes(ctypes.byref(_ext_p(num_heads=20))) == ctypes.c_size_t(-1).value
+
+
+def test_product_path_never_loads_the_oracle():
+    """Importing the package (and the benchmark's helpers it needs) loads libmlaq.so and
+    nothing from oracle/: no CPU path stands behind the calls.  The package source names no
+    oracle module either."""
+    code = ("import sys; import quantized_kv_paged_amd as qk; "
+            "bad = [m for m in sys.modules if m == 'oracle' or m.startswith('oracle.')]; "
+            "print(qk.LIB_PATH); assert not bad, bad")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip().endswith("libmlaq.so")
+    pkg = os.path.join(ROOT, "quantized_kv_paged_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"\bimport\s+oracle|\bfrom\s+oracle\b", text), f
