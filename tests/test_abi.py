@@ -249,3 +249,14 @@ def test_product_path_never_loads_the_oracle():
             if f.endswith((".py", ".cpp", ".hip", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"\bimport\s+oracle|\bfrom\s+oracle\b", text), f
+
+
+def test_oracle_shares_nothing_with_the_hip_path():
+    """oracle/ imports, includes and links nothing from the GPU package (its C twin is built
+    from its own source only)."""
+    odir = os.path.join(ROOT, "oracle")
+    for f in os.listdir(odir):
+        if f.endswith((".py", ".c", ".h")):
+            text = open(os.path.join(odir, f)).read()
+            assert not re.search(r"import\s+quantized_kv_paged_amd|from\s+quantized_kv_paged_amd|libmlaq|csrc/|mlaq\.h",
+                                 text), f
