@@ -87,6 +87,17 @@ def test_extend_request_with_empty_chunk():
     _run([100, 50, 0], [3, 0, 7], 64, seed=58, splits=(0, 2))
 
 
+def test_prefill_many_blocks_32_heads():
+    """Causal prompts of unequal lengths with more token blocks than CUs (600 workgroups),
+    32 heads, one and two KV splits."""
+    _run([0, 0, 0, 0], [300, 257, 64, 1], 64, seed=59, splits=(0, 2), heads=32)
+
+
+def test_extend_many_blocks_128_heads():
+    """Long chunks over a cached prefix with eight head groups (528 workgroups), KV splits."""
+    _run([300, 40], [130, 129], 64, seed=60, splits=(0, 3), heads=128)
+
+
 def test_extend_32_heads():
     _run([300], [20], 64, seed=53, heads=32)
 
