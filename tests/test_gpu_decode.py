@@ -99,6 +99,27 @@ def test_page_placement_is_bitwise_invariant():
         assert np.array_equal(o1, o2) and np.array_equal(l1, l2), s
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "nvfp4"])
+def test_request_order_is_bitwise_invariant(fmt):
+    """A request's result depends on nothing but its own query, length and rows: reversing the
+    batch order (queries, lengths and page-table segments together) reverses the outputs bit
+    for bit, with the automatic split count and with forced ones."""
+    c = build_case(fmt, [333, 0, 1500, 64, 17], 64, seed=23)
+    d = Device(c)
+    B = len(c.pt.kv_lens)
+    seg = [c.pt.kv_indices[c.pt.kv_indptr[b]:c.pt.kv_indptr[b + 1]] for b in range(B)]
+    order = list(range(B))[::-1]
+    d2 = Device(c)
+    d2.q = d.q[order].contiguous()
+    d2.lens = d.lens[order].contiguous()
+    d2.indices = torch.from_numpy(np.concatenate([seg[b] for b in order]).astype(np.int32)).cuda()
+    d2.indptr = torch.from_numpy(np.concatenate([[0], np.cumsum([len(seg[b]) for b in order])]).astype(np.int32)).cuda()
+    for s in (0, 1, 3):
+        o1, l1 = gpu_decode(c, d, num_splits=s)
+        o2, l2 = gpu_decode(c, d2, num_splits=s)
+        assert np.array_equal(o1[order], o2) and np.array_equal(l1[order], l2), s
+
+
 def test_fp8_and_nvfp4_agree_on_shared_values():
     """An FP8 pool and an NVFP4 pool (all block scales 1.0, global scale 1.0) holding the same
     E2M1 values dequantize to the same fp16 operands.  The two formats run different workgroup
