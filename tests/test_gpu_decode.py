@@ -120,6 +120,22 @@ def test_request_order_is_bitwise_invariant(fmt):
         assert np.array_equal(o1[order], o2) and np.array_equal(l1[order], l2), s
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "nvfp4"])
+def test_head_groups_are_independent(fmt):
+    """With 64 heads, each 16-head group gives bit for bit what a 16-head call on the same
+    query rows gives (same forced split count): the head groups share nothing but the rows."""
+    c = build_case(fmt, [900, 5, 260], 64, seed=25, heads=64)
+    d = Device(c)
+    for s in (1, 4):
+        o_all, l_all = gpu_decode(c, d, num_splits=s)
+        for hg in range(4):
+            d16 = Device(c)
+            d16.q = d.q[:, 16 * hg:16 * (hg + 1)].contiguous()
+            o, l = gpu_decode(c, d16, num_splits=s)
+            assert np.array_equal(o, o_all[:, 16 * hg:16 * (hg + 1)]), (s, hg)
+            assert np.array_equal(l, l_all[:, 16 * hg:16 * (hg + 1)]), (s, hg)
+
+
 def test_fp8_and_nvfp4_agree_on_shared_values():
     """An FP8 pool and an NVFP4 pool (all block scales 1.0, global scale 1.0) holding the same
     E2M1 values dequantize to the same fp16 operands.  The two formats run different workgroup
