@@ -98,6 +98,13 @@ def test_extend_many_blocks_128_heads():
     _run([300, 40], [130, 129], 64, seed=60, splits=(0, 3), heads=128)
 
 
+@pytest.mark.parametrize("page_size", [1, 32, 128])
+def test_extend_page_sizes(page_size):
+    """The workspace gather and the chunk write at other page sizes, one-token pages included;
+    chunks start mid-page and cross page edges."""
+    _run([0, 130, 75], [9, 40, 64], page_size, seed=61 + page_size, splits=(0, 2))
+
+
 def test_extend_32_heads():
     _run([300], [20], 64, seed=53, heads=32)
 
