@@ -284,7 +284,7 @@ def main():
     fcode = qk.MLAQ_FP8_E4M3 if fmt == "fp8" else qk.MLAQ_NVFP4
     splits = qk.mlaq_decode_num_splits(p, fcode)
     # one workspace large enough for every format run on this shape (the comparison legs)
-    need = max([qk.mlaq_decode_workspace_bytes(p, f) for f in (qk.MLAQ_FP8_E4M3, qk.MLAQ_NVFP4, qk.MLAQ_BF16)] +
+    need = max([qk.mlaq_decode_workspace_bytes(p)] +
                [qk._lib.mlaq_decode_nvfp4_append_workspace_bytes(ctypes.byref(p))])
     ws = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
     out = torch.empty((w.batch, w.heads, 512), dtype=torch.float32, device="cuda")

@@ -60,7 +60,14 @@ extern "C" {
 #define MLAQ_NVFP4_DATA_BYTES 288
 #define MLAQ_NVFP4_SCALE_BYTES 36
 #define MLAQ_MAX_SPLITS 1024
-#define MLAQ_MAX_KV_LEN (1 << 26)
+#define MLAQ_MAX_KV_LEN (1 << 24)
+/* Longest KV chunk one split may cover.  Probabilities enter the PV products as fp16 relative to
+ * the chunk's running maximum, so a token far below that maximum rounds on the fp16 subnormal grid
+ * (absolute error at most 2^-25 of the largest weight); capping the chunk bounds the sum of those
+ * errors by 2^14 * 2^-25 = 2^-11 of the largest weight, the size of ordinary fp16 rounding.  A
+ * forced num_splits must therefore satisfy max_kv_len <= num_splits * MLAQ_MAX_SPLIT_TOKENS, and
+ * the automatic plan always does. */
+#define MLAQ_MAX_SPLIT_TOKENS (1 << 14)
 
 typedef enum {
   MLAQ_OK = 0,
@@ -68,43 +75,61 @@ typedef enum {
   MLAQ_ERR_SHAPE = 2,       /* a size is out of the supported range */
   MLAQ_ERR_ALIGN = 3,       /* a pointer is not aligned as documented */
   MLAQ_ERR_UNSUPPORTED = 4, /* format combination not implemented */
-  MLAQ_ERR_WORKSPACE = 5,   /* workspace smaller than mlaq_decode_workspace_bytes() */
+  MLAQ_ERR_WORKSPACE = 5,   /* workspace smaller than the size the call needs */
   MLAQ_ERR_LAUNCH = 6,      /* the HIP launch itself failed */
-  MLAQ_ERR_VALUE = 7        /* a scalar argument is not finite / not positive */
+  MLAQ_ERR_VALUE = 7        /* a scalar argument is not finite / not positive (a scale of 0 or NaN
+                               would make every output NaN without an error) */
 } mlaq_status;
 
 typedef enum { MLAQ_BF16 = 0, MLAQ_FP8_E4M3 = 1, MLAQ_NVFP4 = 2, MLAQ_FP32 = 3 } mlaq_format;
 
+/* The host-side inputs of the decode plan ("The Smoking Gun: Tracing the FP8-to-BF16 KV Cache
+ * Cast", section "Message Overview": plan() receives the head count, kv_lora_rank 512 + rope 64,
+ * page size, sm_scale and host copies of the lengths). */
 typedef struct {            /* (host) */
   int32_t batch;            /* >= 0; 0 is a no-op */
   int32_t num_heads;        /* multiple of 16, 16 .. 128 */
   int32_t page_size;        /* tokens per page: a power of two, 1 .. 1024 */
-  int32_t max_kv_len;       /* host upper bound of kv_lens[] (split planning), 0 .. MLAQ_MAX_KV_LEN */
   int64_t pool_tokens;      /* rows in the pool (> 0) */
-  int32_t num_splits;       /* KV chunks per request; 0 = choose automatically */
+  int32_t max_kv_len;       /* host upper bound of kv_lens[] (split planning), 0 .. MLAQ_MAX_KV_LEN */
+  int32_t num_splits;       /* KV chunks per request; 0 = choose automatically; a forced count
+                               must satisfy max_kv_len <= num_splits * MLAQ_MAX_SPLIT_TOKENS */
   float sm_scale;           /* multiplies q . k before the softmax; finite */
 } mlaq_decode_params;
 
-/* (host) Splits a decode of the given KV format (MLAQ_FP8_E4M3, MLAQ_NVFP4 or MLAQ_BF16, the
- * format of the decode call that will use them) will use for these parameters (resolves
- * num_splits = 0), or 0 if the parameters or the format are invalid.  The plan depends on
- * the format because the formats run different workgroup shapes.  Host arguments only. */
+/* (host) Workspace bytes that serve a decode of any KV format (FP8, NVFP4, BF16) with these
+ * parameters: the largest of mlaq_decode_format_workspace_bytes over the three formats.  0 when
+ * no format needs one (one split each), SIZE_MAX if the parameters are invalid.  The workspace
+ * holds one fp32 partial output plus running max and sum per (request, split, 16-head group)
+ * (the split-KV partials of the decode plan, same passage as mlaq_decode_params); it must be
+ * 256-byte aligned. */
+size_t mlaq_decode_workspace_bytes(const mlaq_decode_params* p);
+
+/* (host) The exact workspace bytes a decode of one KV format (MLAQ_FP8_E4M3, MLAQ_NVFP4 or
+ * MLAQ_BF16) needs; the formats run different workgroup shapes and so plan different split
+ * counts.  SIZE_MAX if the parameters or the format are invalid. */
+size_t mlaq_decode_format_workspace_bytes(const mlaq_decode_params* p, mlaq_format kv_format);
+
+/* (host) Splits a decode of the given KV format will use for these parameters (resolves
+ * num_splits = 0), or 0 if the parameters or the format are invalid.  Host arguments only. */
 int32_t mlaq_decode_num_splits(const mlaq_decode_params* p, mlaq_format kv_format);
 
-/* (host) Workspace bytes a decode of the given KV format with these parameters needs (0 when it needs none,
- * which is the case for a single split), or SIZE_MAX if the parameters are invalid.
- * The workspace holds one fp32 partial output plus running max and sum per
- * (request, split, 16-head group); it must be 256-byte aligned. */
-size_t mlaq_decode_workspace_bytes(const mlaq_decode_params* p, mlaq_format kv_format);
-
-/* Decode over an FP8 e4m3fn pool.  kv_scale (> 0, finite) is the per-tensor dequant
- * multiplier: k = e4m3(code) * kv_scale.  Alignment: q, kv, out 16 B; lse 4 B. */
+/* Decode over an FP8 e4m3fn pool, dequantized inside the kernel: the pool the pages' server
+ * kept in float8_e4m3fn and cast whole to BF16 before every decode ("The Smoking Gun: Tracing the
+ * FP8-to-BF16 KV Cache Cast", section "The Investigation Leading to This Message"; "The FP8 KV
+ * Cache Wall", section "Context and Motivation"), here read as stored.  kv_scale (> 0, finite) is
+ * the per-tensor dequant multiplier: k = e4m3(code) * kv_scale.  Workspace: at least
+ * mlaq_decode_format_workspace_bytes(p, MLAQ_FP8_E4M3) (mlaq_decode_workspace_bytes(p) always
+ * suffices).  Alignment: q, kv, out 16 B; lse 4 B. */
 mlaq_status mla_decode_fp8(const mlaq_decode_params* p, const uint16_t* q, const uint8_t* kv, float kv_scale,
                            const int32_t* kv_indptr, const int32_t* kv_indices, const int32_t* kv_lens,
                            float* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Decode over an NVFP4 pool: k = e2m1(code) * e4m3(block scale) * global_scale.
- * Alignment: q, kv_data, out 16 B; kv_scales 4 B; lse 4 B. */
+/* Decode over an NVFP4 pool read as stored (NVFP4 article on aitop.news, implementation item 3:
+ * packed tiles and E4M3 block scales converted in the kernel, the global scale applied as a scalar
+ * factor; format section: k = e2m1(code) * e4m3(block scale) * global_scale).  Workspace: at least
+ * mlaq_decode_format_workspace_bytes(p, MLAQ_NVFP4).  Alignment: q, kv_data, out 16 B; kv_scales
+ * 4 B; lse 4 B. */
 mlaq_status mla_decode_nvfp4(const mlaq_decode_params* p, const uint16_t* q, const uint8_t* kv_data,
                              const uint8_t* kv_scales, float global_scale, const int32_t* kv_indptr,
                              const int32_t* kv_indices, const int32_t* kv_lens, float* out, float* lse,
@@ -170,8 +195,11 @@ mlaq_status mla_extend_nvfp4(const mlaq_extend_params* p, const uint16_t* q, con
                              const int32_t* prefix_lens, const int64_t* slot_mapping, float* out, float* lse,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Decode over a BF16 pool (the comparison path that first casts an FP8 pool to BF16,
- * as the pages' server did, and a cross-check of the quantized paths). */
+/* Decode over a BF16 pool: the second half of the path the pages' server ran, which cast the
+ * FP8 pool to BF16 and then decoded in BF16 ("The Smoking Gun: Tracing the FP8-to-BF16 KV Cache
+ * Cast", section "The Investigation Leading to This Message"), kept as the comparison baseline and
+ * as a cross-check of the quantized paths.  Workspace: at least
+ * mlaq_decode_format_workspace_bytes(p, MLAQ_BF16).  Alignment: q, kv, out 16 B; lse 4 B. */
 mlaq_status mla_decode_bf16(const mlaq_decode_params* p, const uint16_t* q, const uint16_t* kv,
                             const int32_t* kv_indptr, const int32_t* kv_indices, const int32_t* kv_lens,
                             float* out, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream);
@@ -188,19 +216,27 @@ mlaq_status kv_quantize_nvfp4(const void* src, mlaq_format src_format, float src
                               const int64_t* slot_mapping, uint8_t* kv_data, uint8_t* kv_scales,
                               int64_t pool_tokens, float global_scale, hipStream_t stream);
 
-/* Dequantize pool rows into a dense buffer dst [num_rows, 576].
+/* Dequantize pool rows into a dense buffer dst [num_rows, 576]: the whole-pool FP8 -> BF16 cast of
+ * the pages' server ("The Smoking Gun: Tracing the FP8-to-BF16 KV Cache Cast", section "The
+ * Investigation Leading to This Message"), the cast of only the active rows that was its first fix
+ * ("The FP8 KV Cache Wall", sections "The Message" and "Aftermath"), and the NVFP4 -> FP8 prefix
+ * workspace of extend (NVFP4 article on aitop.news, implementation item 2).
  * src_format MLAQ_FP8_E4M3: value = e4m3(code) * scale (kv_scales must be NULL);
  * src_format MLAQ_NVFP4:    value = e2m1 * e4m3(block scale) * scale.
  * The fp32 value is fl32(fl32(e2m1 * e4m3) * scale) (fl32(e4m3 * scale) for FP8);
  * dst_format MLAQ_FP32 stores it, MLAQ_BF16 rounds it to nearest even, MLAQ_FP8_E4M3
  * re-encodes it (nearest even, saturating at 448; NVFP4 source only).
- * rows: int64 [num_rows] pool rows to read (each < pool_tokens, else the output row is
- * NaN), or NULL for rows 0 .. num_rows-1.  kv_data and dst 16-B aligned. */
+ * rows: int64 [num_rows] pool rows to read (each in [0, pool_tokens), else the output row is
+ * NaN), or NULL for rows 0 .. num_rows-1.  pool_tokens (the rows of kv_data) is what lets a
+ * device-resident row list be range-checked without a fault.  kv_data and dst 16-B aligned. */
 mlaq_status kv_dequantize(mlaq_format src_format, const uint8_t* kv_data, const uint8_t* kv_scales, float scale,
                           const int64_t* rows, int64_t num_rows, int64_t pool_tokens, mlaq_format dst_format,
                           void* dst, hipStream_t stream);
 
-/* (host) Profiling hook for callers that time the kernels themselves.  Registers up to four
+/* ---- Measurement aids (not steps of the path) ---- */
+
+/* (host) Profiling hook for callers that time the kernels themselves, and the one piece of
+ * thread-local state besides the error message.  Registers up to four
  * HIP events (hipEvent_t, or NULL) for the NEXT decode call made on this thread: the split-KV
  * kernel is launched with `split_start` / `split_end` recorded at its own start and end
  * (hipExtLaunchKernelGGL), and the merge kernel, if the call runs one, with `merge_start` /

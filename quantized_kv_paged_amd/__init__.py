@@ -28,7 +28,7 @@ if not os.path.exists(LIB_PATH):
 
 class DecodeParams(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("num_heads", ctypes.c_int32), ("page_size", ctypes.c_int32),
-                ("max_kv_len", ctypes.c_int32), ("pool_tokens", ctypes.c_int64), ("num_splits", ctypes.c_int32),
+                ("pool_tokens", ctypes.c_int64), ("max_kv_len", ctypes.c_int32), ("num_splits", ctypes.c_int32),
                 ("sm_scale", ctypes.c_float)]
 
 
@@ -44,7 +44,8 @@ _pp = ctypes.POINTER(DecodeParams)
 _ep = ctypes.POINTER(ExtendParams)
 _SIGS = {
     "mlaq_decode_num_splits": ([_pp, ctypes.c_int], _i32),
-    "mlaq_decode_workspace_bytes": ([_pp, ctypes.c_int], _sz),
+    "mlaq_decode_workspace_bytes": ([_pp], _sz),
+    "mlaq_decode_format_workspace_bytes": ([_pp, ctypes.c_int], _sz),
     "mla_decode_fp8": ([_pp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "mla_decode_nvfp4": ([_pp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "mla_decode_bf16": ([_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
@@ -105,21 +106,27 @@ def last_error() -> str:
 
 
 def decode_params(batch, num_heads, page_size, max_kv_len, pool_tokens, sm_scale, num_splits=0) -> DecodeParams:
-    return DecodeParams(batch, num_heads, page_size, max_kv_len, pool_tokens, num_splits, sm_scale)
+    return DecodeParams(batch=batch, num_heads=num_heads, page_size=page_size, pool_tokens=pool_tokens,
+                        max_kv_len=max_kv_len, num_splits=num_splits, sm_scale=sm_scale)
 
 
 def mlaq_decode_num_splits(p: DecodeParams, kv_format: int) -> int:
     return _lib.mlaq_decode_num_splits(ctypes.byref(p), kv_format)
 
 
-def mlaq_decode_workspace_bytes(p: DecodeParams, kv_format: int) -> int:
-    n = _lib.mlaq_decode_workspace_bytes(ctypes.byref(p), kv_format)
+def mlaq_decode_workspace_bytes(p: DecodeParams, kv_format: int | None = None) -> int:
+    """Workspace bytes of a decode with params p: for one KV format, or (kv_format None) the size
+    that serves every decode format."""
+    if kv_format is None:
+        n = _lib.mlaq_decode_workspace_bytes(ctypes.byref(p))
+    else:
+        n = _lib.mlaq_decode_format_workspace_bytes(ctypes.byref(p), kv_format)
     if n == ctypes.c_size_t(-1).value:
         raise MlaqError(2, last_error())
     return n
 
 
-def alloc_workspace(p: DecodeParams, kv_format: int, device="cuda") -> torch.Tensor | None:
+def alloc_workspace(p: DecodeParams, kv_format: int | None = None, device="cuda") -> torch.Tensor | None:
     n = mlaq_decode_workspace_bytes(p, kv_format)
     return torch.empty(n, dtype=torch.uint8, device=device) if n else None
 

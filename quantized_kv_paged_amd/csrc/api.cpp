@@ -30,6 +30,11 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 bool finite_pos(float x) { return std::isfinite(x) && x > 0.0f; }
 
 
+// Fewest splits whose chunks stay within MLAQ_MAX_SPLIT_TOKENS (the fp16 probability range).
+int min_splits(int64_t max_kv_len) {
+  return (int)std::max<int64_t>(1, (max_kv_len + MLAQ_MAX_SPLIT_TOKENS - 1) / MLAQ_MAX_SPLIT_TOKENS);
+}
+
 // Split planning.  Every workgroup processes one (request, chunk, 16-head group) in tiles of
 // the format's tile size; with all requests at the host-known bound, workgroups run in
 // "rounds" of the resident slots (CUs x workgroups per CU).  The cost (in tile-times) is
@@ -42,10 +47,11 @@ int plan_splits(int fmt, int batch, int head_groups, int max_kv_len) {
   const int tiles = (max_kv_len + tile - 1) / tile;
   if (tiles <= 1 || batch <= 0) return 1;
   const double fixed = 0.5, merge = 0.5;
-  int best = 1;
+  const int smin = min_splits(max_kv_len);
+  int best = smin;
   double best_cost = std::numeric_limits<double>::infinity();
   const int smax = tiles < MLAQ_MAX_SPLITS ? tiles : MLAQ_MAX_SPLITS;
-  for (int s = 1; s <= smax; ++s) {
+  for (int s = smin; s <= smax; ++s) {
     const double wgs = (double)batch * head_groups * s;
     const double rounds = std::ceil(wgs / slots);
     const double per = std::ceil((double)tiles / s);
@@ -68,6 +74,10 @@ mlaq_status check_params(const mlaq_decode_params* p) {
     return fail(MLAQ_ERR_SHAPE, "pool_tokens %lld out of range", (long long)p->pool_tokens);
   if (p->num_splits < 0 || p->num_splits > MLAQ_MAX_SPLITS)
     return fail(MLAQ_ERR_SHAPE, "num_splits %d not in [0, %d]", p->num_splits, MLAQ_MAX_SPLITS);
+  if (p->num_splits > 0 && p->num_splits < min_splits(p->max_kv_len))
+    return fail(MLAQ_ERR_SHAPE,
+                "num_splits %d leaves chunks longer than %d tokens (max_kv_len %d needs at least %d splits)",
+                p->num_splits, MLAQ_MAX_SPLIT_TOKENS, p->max_kv_len, min_splits(p->max_kv_len));
   if (!std::isfinite(p->sm_scale)) return fail(MLAQ_ERR_VALUE, "sm_scale is not finite");
   return MLAQ_OK;
 }
@@ -218,9 +228,14 @@ mlaq_status extend_layout(const mlaq_extend_params* p, ExtendLayout& L) {
     const int tile = mlaq::extend_attn_tile_rows(), per_group = mlaq::extend_attn_tokens_per_group();
     const int max_tiles = (int)((span + tile - 1) / tile);
     const int64_t groups = (int64_t)p->batch * ((p->max_chunk_len + per_group - 1) / per_group) * (p->num_heads / 16);
+    // no split may cover more than MLAQ_MAX_SPLIT_TOKENS rows (the fp16 probability range)
+    const int smin = min_splits(span);
+    if (p->num_splits > 0 && p->num_splits < smin)
+      return fail(MLAQ_ERR_SHAPE, "num_splits %d leaves chunks longer than %d rows (%lld rows need at least %d splits)",
+                  p->num_splits, MLAQ_MAX_SPLIT_TOKENS, (long long)span, smin);
     int s_ = p->num_splits > 0 ? p->num_splits
                                : (int)std::min<int64_t>(MLAQ_MAX_SPLITS, groups > 0 ? (mlaq::kComputeUnits + groups - 1) / groups : 1);
-    s_ = std::max(1, std::min(s_, std::max(1, max_tiles)));
+    s_ = std::max(smin, std::max(1, std::min(s_, std::max(1, max_tiles))));
     L.tiles_per_split = std::max(1, (max_tiles + s_ - 1) / s_);
     L.tsplits = (max_tiles + L.tiles_per_split - 1) / L.tiles_per_split;
     if (L.tsplits < 1) L.tsplits = 1;
@@ -255,11 +270,18 @@ int32_t mlaq_decode_num_splits(const mlaq_decode_params* p, mlaq_format kv_forma
   return resolve_splits(fmt, p);
 }
 
-size_t mlaq_decode_workspace_bytes(const mlaq_decode_params* p, mlaq_format kv_format) {
+size_t mlaq_decode_format_workspace_bytes(const mlaq_decode_params* p, mlaq_format kv_format) {
   const int fmt = kv_format_of(kv_format);
   if (fmt < 0) { fail(MLAQ_ERR_UNSUPPORTED, "kv_format %d is not a decode KV format", (int)kv_format); return SIZE_MAX; }
   if (check_params(p) != MLAQ_OK) return SIZE_MAX;
   return workspace_for(p, resolve_splits(fmt, p));
+}
+
+size_t mlaq_decode_workspace_bytes(const mlaq_decode_params* p) {
+  if (check_params(p) != MLAQ_OK) return SIZE_MAX;
+  size_t need = 0;
+  for (int fmt : {mlaq::FMT_FP8, mlaq::FMT_NVFP4, mlaq::FMT_BF16}) need = std::max(need, workspace_for(p, resolve_splits(fmt, p)));
+  return need;
 }
 
 mlaq_status mla_decode_fp8(const mlaq_decode_params* p, const uint16_t* q, const uint8_t* kv, float kv_scale,

@@ -733,13 +733,16 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
 // later batches of partials are loaded one batch ahead of their use.
 constexpr int kMergeThreads = 256;
 constexpr int kMergeUnroll = 4;                                  // splits per group per batch of loads
-constexpr int kMergeMLPer = (MLAQ_MAX_SPLITS + kMergeThreads - 1) / kMergeThreads;   // (m, l) per thread
+// partial slots per (request, head group): up to MLAQ_MAX_SPLITS splits, plus the new token's slot
+// of a fused append
+constexpr int kMergeMaxSlots = MLAQ_MAX_SPLITS + 1;
+constexpr int kMergeMLPer = (kMergeMaxSlots + kMergeThreads - 1) / kMergeThreads;   // (m, l) per thread
 template <int DIMS>
 __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(DecodeArgs a) {
   constexpr int kMergeDims = DIMS;                                 // dims per workgroup
   constexpr int kMergeGroups = kMergeThreads / (kMergeDims / 4);   // split-strided lane groups
   constexpr int kBatch = kMergeGroups * kMergeUnroll;              // splits per batch of loads
-  __shared__ float sw[MLAQ_MAX_SPLITS];
+  __shared__ float sw[kMergeMaxSlots];
   __shared__ __attribute__((aligned(16))) float sred[kMergeGroups][kMergeDims];
   __shared__ float sx[2][4];
   const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;

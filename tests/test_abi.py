@@ -35,12 +35,92 @@ def test_header_functions_are_exported():
     assert set(qk.EXPORTS) == set(names)
 
 
+def _declarations():
+    """{name: (return type, [parameter types])} of every function the header declares."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for ret, name, args in re.findall(r"^\s*((?:const\s+)?[a-z_0-9]+\s*\**)\s*([a-z_0-9]+)\s*\(([^;{]*?)\)\s*;",
+                                      text, flags=re.M | re.S):
+        types = []
+        for a in " ".join(args.split()).split(","):
+            a = a.strip()
+            if a in ("", "void"):
+                continue
+            t = re.sub(r"\s*\b[a-z_0-9]+$", "", a)          # drop the parameter name
+            types.append(re.sub(r"\s*\*", "*", t))
+        out[name] = (re.sub(r"\s*\*", "*", ret.strip()), types)
+    return out
+
+
+# The calls of the boundary as the hot-path scope table writes them (plan() inputs, separate q and
+# KV formats, pool rows of 576, global scale as a scalar), with the documented deviations applied:
+# kv_dequantize takes pool_tokens after num_rows so that a device-resident row list can be
+# range-checked without a fault.
+_BOUNDARY = {
+    "mlaq_decode_workspace_bytes": ("size_t", ["const mlaq_decode_params*"]),
+    "mla_decode_fp8": ("mlaq_status", ["const mlaq_decode_params*", "const uint16_t*", "const uint8_t*", "float",
+                                       "const int32_t*", "const int32_t*", "const int32_t*", "float*", "float*",
+                                       "void*", "size_t", "hipStream_t"]),
+    "mla_decode_nvfp4": ("mlaq_status", ["const mlaq_decode_params*", "const uint16_t*", "const uint8_t*",
+                                         "const uint8_t*", "float", "const int32_t*", "const int32_t*",
+                                         "const int32_t*", "float*", "float*", "void*", "size_t", "hipStream_t"]),
+    "mla_decode_bf16": ("mlaq_status", ["const mlaq_decode_params*", "const uint16_t*", "const uint16_t*",
+                                        "const int32_t*", "const int32_t*", "const int32_t*", "float*", "float*",
+                                        "void*", "size_t", "hipStream_t"]),
+    "kv_quantize_nvfp4": ("mlaq_status", ["const void*", "mlaq_format", "float", "int64_t", "const int64_t*",
+                                          "uint8_t*", "uint8_t*", "int64_t", "float", "hipStream_t"]),
+    "kv_dequantize": ("mlaq_status", ["mlaq_format", "const uint8_t*", "const uint8_t*", "float", "const int64_t*",
+                                      "int64_t", "int64_t", "mlaq_format", "void*", "hipStream_t"]),
+    "mlaq_last_error": ("const char*", []),
+}
+# Calls beyond the table, each documented in the header: the per-format sizes and split counts,
+# the fused append, extend / prefill, the allocation-free decode, and the measurement aids.
+_ADDED = {"mlaq_decode_format_workspace_bytes", "mlaq_decode_num_splits", "mla_decode_nvfp4_append",
+          "mlaq_decode_nvfp4_append_workspace_bytes", "mla_extend_nvfp4", "mlaq_extend_workspace_bytes",
+          "mlaq_extend_num_splits", "mlaq_set_profile_events", "mlaq_read_probe", "mlaq_version",
+          "mla_decode_nvfp4_noalloc", "mlaq_noalloc_max_bytes"}
+
+
+def test_boundary_signatures():
+    decl = _declarations()
+    for name, sig in _BOUNDARY.items():
+        assert decl.get(name) == sig, (name, decl.get(name))
+    extra = set(decl) - set(_BOUNDARY)
+    assert extra <= _ADDED, extra - _ADDED
+
+
+def test_params_layout_and_status_codes():
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct \{(.*?)\} mlaq_decode_params;", text, flags=re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"([a-z_0-9]+)\s+([a-z_0-9]+)\s*;", body)
+    assert fields == [("int32_t", "batch"), ("int32_t", "num_heads"), ("int32_t", "page_size"),
+                      ("int64_t", "pool_tokens"), ("int32_t", "max_kv_len"), ("int32_t", "num_splits"),
+                      ("float", "sm_scale")]
+    assert [f for f, _ in DecodeParams._fields_] == [n for _, n in fields]
+    # the binding's layout is the C compiler's
+    src = ("#include <stdio.h>\n#include <stddef.h>\n#include \"mlaq.h\"\nint main(void) { printf(\"%zu"
+           + " %zu" * len(fields) + "\\n\", sizeof(mlaq_decode_params)"
+           + "".join(f", offsetof(mlaq_decode_params, {n})" for _, n in fields) + "); return 0; }\n")
+    import tempfile
+    with tempfile.TemporaryDirectory() as td:
+        c, exe = os.path.join(td, "l.c"), os.path.join(td, "l")
+        open(c, "w").write(src)
+        r = subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                            "-I", "/opt/rocm/include", c, "-o", exe], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+        got = [int(x) for x in subprocess.run([exe], capture_output=True, text=True).stdout.split()]
+    assert got == [ctypes.sizeof(DecodeParams)] + [getattr(DecodeParams, n).offset for _, n in fields]
+    codes = dict((n, int(v)) for n, v in re.findall(r"(MLAQ_(?:OK|ERR_[A-Z]+))\s*=\s*(\d+)", text))
+    assert codes == {"MLAQ_OK": 0, "MLAQ_ERR_NULL": 1, "MLAQ_ERR_SHAPE": 2, "MLAQ_ERR_ALIGN": 3,
+                     "MLAQ_ERR_UNSUPPORTED": 4, "MLAQ_ERR_WORKSPACE": 5, "MLAQ_ERR_LAUNCH": 6, "MLAQ_ERR_VALUE": 7}
+
+
 def _p(**kw):
     d = dict(batch=2, num_heads=16, page_size=64, max_kv_len=4096, pool_tokens=1 << 16, num_splits=0,
              sm_scale=0.07)
     d.update(kw)
-    return DecodeParams(d["batch"], d["num_heads"], d["page_size"], d["max_kv_len"], d["pool_tokens"],
-                        d["num_splits"], d["sm_scale"])
+    return DecodeParams(**d)
 
 
 FAKE = 1 << 20  # a 256-byte aligned fake device address; never dereferenced on these paths
@@ -77,7 +157,7 @@ def test_pointer_and_value_validation():
     assert _fp8(p, scale=float("inf")) == ERR_VALUE
     assert _fp8(p, ws=None) == ERR_NULL
     need = qk.mlaq_decode_workspace_bytes(p, qk.MLAQ_FP8_E4M3)
-    assert need > 0
+    assert need > 0 and qk.mlaq_decode_workspace_bytes(p) >= need
     assert _fp8(p, ws_bytes=need - 1) == ERR_WORKSPACE
     assert _fp8(p, ws=FAKE + 16) == ERR_ALIGN
     assert "workspace" in qk.last_error()
@@ -150,6 +230,38 @@ def test_split_planning_and_workspace():
     assert qk.mlaq_decode_num_splits(_p(), qk.MLAQ_FP32) == 0          # not a decode KV format
     with pytest.raises(MlaqError):
         qk.mlaq_decode_workspace_bytes(_p(), qk.MLAQ_FP32)
+    # the format-free size serves every format
+    for name, w in synth.WORKLOADS.items():
+        p = _p(batch=w.batch, num_heads=w.heads, page_size=w.page_size, max_kv_len=w.kv_len,
+               pool_tokens=w.pool_tokens)
+        assert qk.mlaq_decode_workspace_bytes(p) == max(
+            qk.mlaq_decode_workspace_bytes(p, f) for f in (qk.MLAQ_FP8_E4M3, qk.MLAQ_NVFP4, qk.MLAQ_BF16))
+    with pytest.raises(MlaqError):
+        qk.mlaq_decode_workspace_bytes(_p(num_heads=20))
+
+
+def test_split_token_cap():
+    """No split covers more than MLAQ_MAX_SPLIT_TOKENS tokens: forced counts below
+    ceil(max_kv_len / cap) are rejected before any launch, and the automatic plan never goes there."""
+    cap = 1 << 14
+    for L in (cap, cap + 1, 65536, 1 << 20, 1 << 24):
+        need = -(-L // cap)
+        for fmt in (qk.MLAQ_FP8_E4M3, qk.MLAQ_NVFP4, qk.MLAQ_BF16):
+            for b in (1, 2, 64):
+                s = qk.mlaq_decode_num_splits(_p(batch=b, max_kv_len=L), fmt)
+                assert s >= need and -(-L // s) <= cap, (L, fmt, b, s)
+        if need > 1:
+            assert _fp8(_p(max_kv_len=L, num_splits=need - 1)) == ERR_SHAPE
+            assert "splits" in qk.last_error()
+            assert qk.mlaq_decode_num_splits(_p(max_kv_len=L, num_splits=need - 1), qk.MLAQ_NVFP4) == 0
+        assert qk.mlaq_decode_num_splits(_p(max_kv_len=L, num_splits=need), qk.MLAQ_NVFP4) == need
+    assert _fp8(_p(max_kv_len=(1 << 24) + 1)) == ERR_SHAPE              # above MLAQ_MAX_KV_LEN
+    # extend: rows seen per split are capped the same way
+    big = _ext_p(max_prefix_len=65536 - 32, max_chunk_len=32)
+    assert qk._lib.mlaq_extend_num_splits(ctypes.byref(big)) >= 4
+    assert _ext(_ext_p(max_prefix_len=65536 - 32, max_chunk_len=32, num_splits=3)) == ERR_SHAPE
+    assert qk._lib.mlaq_extend_num_splits(ctypes.byref(_ext_p(max_prefix_len=65536 - 32, max_chunk_len=32,
+                                                              num_splits=4))) == 4
 
 
 def _app(p, new_kv=FAKE, fmt=0, src_scale=1.0, data=FAKE, scales=FAKE, g=1.0, ws=FAKE, ws_bytes=1 << 30):

@@ -221,3 +221,49 @@ def test_full_pool_cast_baseline_matches():
     torch.cuda.synchronize()
     ref_out, ref_lse = oracle_decode(c)
     assert_parity(out.double().cpu().numpy(), lse.double().cpu().numpy(), ref_out, ref_lse, tag="cast baseline")
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "nvfp4"])
+def test_peaked_softmax_with_long_tail(fmt):
+    """Probabilities enter the PV products as fp16 relative to the running maximum, so a tail far
+    below one dominant token sits on the fp16 subnormal grid.  One sink token about 20 log2 units
+    above a 64K-token tail that still holds several percent of the weight: automatic splits and the
+    fewest splits the per-split token cap (MLAQ_MAX_SPLIT_TOKENS) admits must match the oracle, and a
+    count below that cap is rejected before any launch."""
+    import quantized_kv_paged_amd as qk
+    from oracle import attention, codecs
+    from oracle import nvfp4 as onv
+    L = 65536
+    c = build_case("fp8", [L], 64, seed=31, sigma=0.5, extra_pages=1)
+    rng = np.random.default_rng(31)
+    u = rng.standard_normal(576)
+    qf = u[None, :] + 0.3 * rng.standard_normal((16, 576))
+    c.q_bits = codecs.bf16_round_bits(qf.astype(np.float32))[None]
+    rows = attention.gather_rows(c.pt.kv_indptr, c.pt.kv_indices, 64, 0, L)
+    sink = int(rows[40000])
+    c.fp8_pool[sink] = torch.from_numpy((0.33 * u).astype(np.float32)).to(torch.float8_e4m3fn).view(
+        torch.uint8).numpy()
+    if fmt == "nvfp4":
+        c.fmt = "nvfp4"
+        c.nv_data, c.nv_scales = onv.quantize_fp8_rows(c.fp8_pool, 1.0, 1.0)
+        c.scale = 1.0
+    # the regime: gap of the sink over the tail's typical score, and the tail's share of the weight
+    x = cases.dequant_rows(c, rows)
+    s = codecs.bf16_bits_to_f64(c.q_bits[0]) @ x.T * c.w.sm_scale / np.log(2)      # log2 units [16, L]
+    gap = s[:, 40000] - np.median(np.delete(s, 40000, axis=1), axis=1)
+    w_ = np.exp2(s - s.max(axis=1, keepdims=True))
+    tail = 1.0 - w_[:, 40000] / w_.sum(axis=1)
+    assert 17 <= gap.min() and gap.max() <= 25 and tail.min() > 0.02, (gap, tail)
+    ref_out, ref_lse = oracle_decode(c)
+    d = Device(c)
+    fcode = qk.MLAQ_FP8_E4M3 if fmt == "fp8" else qk.MLAQ_NVFP4
+    p = qk.decode_params(1, 16, 64, L, c.fp8_pool.shape[0], c.w.sm_scale, 0)
+    least = -(-L // (1 << 14))
+    for splits in (0, least):
+        out, lse = gpu_decode(c, d, num_splits=splits)
+        mx, rel = assert_parity(out, lse, ref_out, ref_lse, tag=f"sink {fmt} splits={splits}")
+        print(f"[sink {fmt}] gap {gap.min():.1f}-{gap.max():.1f} log2, tail weight {tail.min():.3f}-{tail.max():.3f}; "
+              f"splits={splits or qk.mlaq_decode_num_splits(p, fcode)} max-abs {mx:.2e} rel-L2 {rel:.2e}", flush=True)
+    with pytest.raises(qk.MlaqError) as e:
+        gpu_decode(c, d, num_splits=least - 1)
+    assert e.value.status == 2

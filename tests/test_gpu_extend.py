@@ -138,3 +138,59 @@ def test_initial_prefill_is_extend_with_empty_prefix():
     """The initial-prefill path of the pages (attention over the chunk's own FP8 KV, then the NVFP4
     write; no cache read) is extend with every prefix empty: causal attention inside each prompt."""
     _run([0, 0, 0], [1, 70, 257], 64, seed=55, splits=(0, 2))
+
+
+@pytest.mark.parametrize("kind", ["extend", "prefill"])
+def test_benchmark_shapes(kind):
+    """The launch configurations the benchmark times, on 32K NVFP4 contexts (g = 1): extend = 4
+    requests x a 256-token chunk after a 32,512-token prefix; prefill = 4 prompts of 2,048 tokens
+    (empty prefixes).  Every request's FP8 workspace region is checked bit for bit, the cache after
+    the chunk write bit for bit (written rows and every other row), and the attention of the first,
+    the last and every 16th chunk token of every request (all heads) against the oracle."""
+    import dataclasses
+    import quantized_kv_paged_amd as qk
+    w = dataclasses.replace(synth.WORKLOADS["nvfp4_32k"], name="extend_bench", batch=4, pool_tokens=4 * 32768)
+    pt = synth.page_table(w)
+    host = synth.build_fp8_pool(w, pt)
+    data_np, scales_np = onv.quantize_fp8_rows(host, 1.0, 1.0)
+    del host
+    B, P, H = 4, w.page_size, w.heads
+    C, PF, qseed, kseed = (256, w.kv_len - 256, w.seed + 7, w.seed) if kind == "extend" else \
+        (2048, 0, w.seed + 8, w.seed + 1)
+    nq = B * C
+    tok = np.arange(PF, PF + C, dtype=np.int64)
+    slots = np.concatenate([pt.kv_indices[pt.kv_indptr[b] + tok // P].astype(np.int64) * P + tok % P
+                            for b in range(B)])
+    q_bits = synth.q_bits(qseed, nq, H)
+    ckv = synth.to_fp8_bytes(synth.extend_chunk_rows(kseed, nq))
+    qo = (np.arange(B + 1) * C).astype(np.int32)
+    p = qk.extend_params(B, H, P, w.pool_tokens, nq, PF, C, w.sm_scale)
+    print(f"[{kind}] {B} x ({PF} prefix + {C} chunk), {qk._lib.mlaq_extend_num_splits(__import__('ctypes').byref(p))}"
+          f" KV splits", flush=True)
+    ws = torch.zeros(qk.mlaq_extend_workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    data, scales = _t(data_np), _t(scales_np)
+    out, lse = qk.mla_extend_nvfp4(_t(q_bits.view(np.int16)).view(torch.bfloat16), _t(qo), _t(ckv), 1.0, data,
+                                   scales, 1.0, _t(pt.kv_indptr), _t(pt.kv_indices),
+                                   _t(np.full(B, PF, np.int32)), _t(slots), P, PF, C, w.sm_scale, workspace=ws)
+    torch.cuda.synchronize()
+    out, lse, wsh = out.double().cpu().numpy(), lse.double().cpu().numpy(), ws.cpu().numpy()
+    region = -(-(PF + C) // 64) * 64
+    q64 = codecs.bf16_bits_to_f64(q_bits)
+    picks = sorted(set([0, C - 1] + list(range(0, C, 16))))
+    got_o, ref_o, got_l, ref_l = [], [], [], []
+    for b in range(B):
+        rows = attention.gather_rows(pt.kv_indptr, pt.kv_indices, P, b, PF)
+        ws_ref = np.concatenate([extend.workspace_prefix(data_np[rows], scales_np[rows], 1.0, 1.0),
+                                 ckv[b * C:(b + 1) * C]])
+        np.testing.assert_array_equal(wsh[b * region * 576:(b * region + PF + C) * 576].reshape(PF + C, 576), ws_ref,
+                                      err_msg=f"{kind} workspace request {b}")
+        x = extend.workspace_values(ws_ref, 1.0)
+        for i in picks:
+            o, l_ = attention.decode_dense(q64[b * C + i], x[:PF + i + 1], w.sm_scale)
+            ref_o.append(o), ref_l.append(l_), got_o.append(out[b * C + i]), got_l.append(lse[b * C + i])
+    mx, rel = assert_parity(np.stack(got_o), np.stack(got_l), np.stack(ref_o), np.stack(ref_l), tag=kind)
+    print(f"[{kind}] {len(got_o)} sampled chunk tokens x {H} heads: max-abs {mx:.2e} rel-L2 {rel:.2e}", flush=True)
+    new_d, new_s = onv.quantize_fp8_rows(ckv, 1.0, 1.0)
+    data_np[slots], scales_np[slots] = new_d, new_s
+    np.testing.assert_array_equal(data.cpu().numpy(), data_np)
+    np.testing.assert_array_equal(scales.cpu().numpy(), scales_np)

@@ -217,3 +217,77 @@ def test_dequantize_fp8_bit_exact():
         out = qk.kv_dequantize(qk.MLAQ_FP8_E4M3, _t(codes), None, scale, qk.MLAQ_BF16)
         _assert_equal_nan_as_class(out.view(torch.int16).cpu().numpy().view(np.uint16), codecs.bf16_round_bits(f32),
                                    qk.MLAQ_BF16)
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.3])
+def test_dequantize_fp8_row_list_bit_exact(scale):
+    """FP8 source through a row list (the gather of the pages' first fix): every listed row, in list
+    order and with repeats, is fl32(e4m3 * scale) (fp32) or its bf16 rounding; rows outside the pool
+    (past the end, negative) give NaN rows."""
+    qk = _qk()
+    rng = np.random.default_rng(43)
+    n = 300
+    codes = rng.integers(0, 256, (n, 576), dtype=np.uint8)
+    rows = rng.integers(0, n, 500).astype(np.int64)
+    rows[[7, 123]] = [n, n + 1000]
+    rows[200] = -1
+    f32 = onv.fp8_rows_to_f32(codes, scale)
+    bad = (rows < 0) | (rows >= n)
+    for fmt in (qk.MLAQ_FP32, qk.MLAQ_BF16):
+        out = qk.kv_dequantize(qk.MLAQ_FP8_E4M3, _t(codes), None, scale, fmt, rows=_t(rows))
+        torch.cuda.synchronize()
+        if fmt == qk.MLAQ_FP32:
+            got, ref = out.cpu().numpy().view(np.uint32), f32.view(np.uint32)
+        else:
+            got, ref = out.view(torch.int16).cpu().numpy().view(np.uint16), codecs.bf16_round_bits(f32)
+        _assert_equal_nan_as_class(got[~bad], ref[rows[~bad]], fmt)
+        assert _nan_mask(got[bad], fmt).all()
+
+
+@pytest.mark.parametrize("kv_scale", [1.0, 0.3])
+def test_gather_then_cast_baseline_end_to_end(kv_scale):
+    """The pages' intermediate fix: the active rows of an FP8 pool gathered and cast to a dense BF16
+    workspace (kv_dequantize with the page table's row list), then the BF16 decode over an identity
+    page table into that workspace.  The workspace is checked bit for bit, the attention against the
+    oracle over the same bf16 values (ragged requests, an empty one, pages of 16 tokens)."""
+    import synth
+    from cases import assert_parity, build_case, oracle_decode, Case
+    from oracle import attention
+    qk = _qk()
+    lens = [700, 0, 33, 1500, 64]
+    P = 16
+    c = build_case("fp8", lens, P, seed=44, sigma=0.5, kv_scale=kv_scale)
+    # active rows of each request, in token order, each request padded to whole pages of the workspace
+    rows, indptr, table = [], [0], []
+    for b, L in enumerate(lens):
+        r = attention.gather_rows(c.pt.kv_indptr, c.pt.kv_indices, P, b, L) if L else np.zeros(0, np.int64)
+        npg = -(-L // P)
+        pad = np.full(npg * P - L, int(r[-1]) if L else 0, dtype=np.int64)
+        base = sum(len(x) for x in rows)
+        rows.append(np.concatenate([r.astype(np.int64), pad]))
+        table.extend(range(base // P, base // P + npg))
+        indptr.append(indptr[-1] + npg)
+    rows = np.concatenate(rows)
+    ws = qk.kv_dequantize(qk.MLAQ_FP8_E4M3, _t(c.fp8_pool), None, kv_scale, qk.MLAQ_BF16, rows=_t(rows))
+    torch.cuda.synchronize()
+    ref_bits = codecs.bf16_round_bits(onv.fp8_rows_to_f32(c.fp8_pool, kv_scale))[rows]
+    np.testing.assert_array_equal(ws.view(torch.int16).cpu().numpy().view(np.uint16), ref_bits)
+    q = torch.from_numpy(c.q_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    ind, ptr = _t(np.array(table, np.int32)), _t(np.array(indptr, np.int32))
+    lens_t = _t(np.array(lens, np.int32))
+    # the oracle over the dense bf16 workspace through the same identity table
+    none = np.zeros(0, np.int32)
+    dense = Case("bf16", c.w, synth.PageTable(np.array(indptr, np.int32), np.array(table, np.int32),
+                                              np.array(lens, np.int32), none, none),
+                 c.q_bits, c.fp8_pool, bf16_pool=ref_bits, max_kv_len=max(lens))
+    ref_out, ref_lse = oracle_decode(dense)
+    for s in (0, 1, 3):
+        out, lse = qk.mla_decode_bf16(q, ws, ptr, ind, lens_t, P, max(lens), c.w.sm_scale, num_splits=s)
+        torch.cuda.synchronize()
+        mx, rel = assert_parity(out.double().cpu().numpy(), lse.double().cpu().numpy(), ref_out, ref_lse,
+                                tag=f"gather-cast scale={kv_scale} splits={s}")
+        print(f"[gather-cast kv_scale={kv_scale}] splits={s} max-abs {mx:.2e} rel-L2 {rel:.2e}", flush=True)
+    # and, at the per-tensor scale of the pages (1.0, where the cast is exact), the oracle over the FP8 pool
+    if kv_scale == 1.0:
+        fo, fl = oracle_decode(c)
+        np.testing.assert_array_equal(fo, ref_out)

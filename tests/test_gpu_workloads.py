@@ -1,7 +1,11 @@
 """Full-size workloads, in the launch configuration the benchmark times (automatic split plan),
-with sampled requests checked against the fp64 oracle (all 16 heads x 512 dims of each
-sampled request).  Pools are generated on the host (FP8 from synth.py, NVFP4 by the
-oracle's encoder), so nothing the oracle reads comes from the GPU path."""
+checked over the WHOLE output: every request, all 16 heads x 512 dims, against the fp64 oracle.
+The gates apply to the whole [B, H, 512] tensor (max-abs 1e-2, relative L2 5e-3) and lse within
+2e-3; the worst per-(request, head) relative L2 is printed, not gated.  Pools are generated on
+the host (FP8 from synth.py, NVFP4 by the oracle's encoder), so nothing the oracle reads comes
+from the GPU path.  The oracle streams each request's rows in 65,536-row chunks."""
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -19,27 +23,36 @@ def _dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def _oracle_request(w, pt, b, dequant):
-    """fp64 oracle for request b, dequantizing its rows chunk by chunk."""
-    L = int(pt.kv_lens[b])
-    q = codecs.bf16_bits_to_f64(synth.q_bits(w.seed, w.batch, w.heads))[b]
+def _oracle_all(w, pt, dequant, workers=8):
+    """fp64 oracle for every request of the batch.  Each request's rows are gathered and dequantized
+    once, in 65,536-row chunks that both passes of the oracle reuse; requests run on a thread pool
+    (the heavy numpy steps release the interpreter lock)."""
+    from concurrent.futures import ThreadPoolExecutor
+    q = codecs.bf16_bits_to_f64(synth.q_bits(w.seed, w.batch, w.heads))
 
-    def chunks():
-        for c0 in range(0, L, CH):
-            rows = attention.gather_rows(pt.kv_indptr, pt.kv_indices, w.page_size, b, L, c0, min(CH, L - c0))
-            yield dequant(rows)
-    return attention.decode_head_block(q, chunks, w.sm_scale)
+    def one(b):
+        L = int(pt.kv_lens[b])
+        xs = [dequant(attention.gather_rows(pt.kv_indptr, pt.kv_indices, w.page_size, b, L, c0, min(CH, L - c0)))
+              for c0 in range(0, L, CH)]
+        return attention.decode_head_block(q[b], lambda: xs, w.sm_scale)
+    with ThreadPoolExecutor(max_workers=min(workers, w.batch)) as ex:
+        res = list(ex.map(one, range(w.batch)))
+    return np.stack([r[0] for r in res]), np.stack([r[1] for r in res])
 
 
 def _check(out, lse, ref_out, ref_lse, tag):
     mx, rel = errors(out, ref_out)
     dl = float(np.abs(lse - ref_lse).max())
-    print(f"[{tag}] max-abs {mx:.2e} rel-L2 {rel:.2e} lse {dl:.2e}", flush=True)
+    diff = (out - ref_out).reshape(out.shape[0] * out.shape[1], -1)
+    per = np.linalg.norm(diff, axis=1) / np.maximum(np.linalg.norm(ref_out.reshape(diff.shape), axis=1), 1e-30)
+    print(f"[{tag}] whole output {out.shape}: max-abs {mx:.2e} rel-L2 {rel:.2e} lse {dl:.2e}; "
+          f"worst per-(request, head) rel-L2 {per.max():.2e}", flush=True)
     assert mx <= TOL_MAX_ABS and rel <= TOL_REL_L2 and dl <= TOL_LSE, tag
 
 
 def _setup(name):
     import quantized_kv_paged_amd as qk
+    t0 = time.perf_counter()
     w = synth.WORKLOADS[name]
     pt = synth.page_table(w)
     host = synth.build_fp8_pool(w, pt)
@@ -47,7 +60,8 @@ def _setup(name):
              indptr=_dev(pt.kv_indptr), indices=_dev(pt.kv_indices), lens=_dev(pt.kv_lens))
     p = qk.decode_params(w.batch, w.heads, w.page_size, w.kv_len, w.pool_tokens, w.sm_scale)
     fmt = qk.MLAQ_NVFP4 if w.fmt == "nvfp4" else qk.MLAQ_FP8_E4M3
-    print(f"[{name}] pool {host.shape}, {qk.mlaq_decode_num_splits(p, fmt)} splits", flush=True)
+    print(f"[{name}] pool {host.shape} generated in {time.perf_counter() - t0:.1f} s, "
+          f"{qk.mlaq_decode_num_splits(p, fmt)} splits", flush=True)
     return qk, w, pt, host, d
 
 
@@ -58,15 +72,18 @@ def _decode_nvfp4(qk, w, d, data, scales, g):
     return out.double().cpu().numpy(), lse.double().cpu().numpy()
 
 
-def test_fp8_32k_pool_of_the_pages():
-    qk, w, pt, host, d = _setup("fp8_32k")
+def _decode_fp8(qk, w, d, host):
     out, lse = qk.mla_decode_fp8(d["q"], _dev(host), 1.0, d["indptr"], d["indices"], d["lens"], w.page_size,
                                  w.kv_len, w.sm_scale)
     torch.cuda.synchronize()
-    out, lse = out.double().cpu().numpy(), lse.double().cpu().numpy()
-    for b in (0, 5):
-        ro, rl = _oracle_request(w, pt, b, lambda rows: onv.dequant_fp8_f64(host[rows], 1.0))
-        _check(out[b], lse[b], ro, rl, f"fp8_32k b={b}")
+    return out.double().cpu().numpy(), lse.double().cpu().numpy()
+
+
+def test_fp8_32k_pool_of_the_pages():
+    qk, w, pt, host, d = _setup("fp8_32k")
+    out, lse = _decode_fp8(qk, w, d, host)
+    ro, rl = _oracle_all(w, pt, lambda rows: onv.dequant_fp8_f64(host[rows], 1.0))
+    _check(out, lse, ro, rl, "fp8_32k, all 8 requests")
 
 
 @pytest.mark.parametrize("calibrated", [False, True])
@@ -77,23 +94,20 @@ def test_nvfp4_32k(calibrated):
     data, scales = onv.quantize_rows(x, g)
     del x
     out, lse = _decode_nvfp4(qk, w, d, data, scales, g)
-    for b in ((0, 43) if not calibrated else (17,)):
-        ro, rl = _oracle_request(w, pt, b, lambda rows: onv.dequant_nvfp4_f64(data[rows], scales[rows], g))
-        _check(out[b], lse[b], ro, rl, f"nvfp4_32k g={g} b={b}")
+    ro, rl = _oracle_all(w, pt, lambda rows: onv.dequant_nvfp4_f64(data[rows], scales[rows], g))
+    _check(out, lse, ro, rl, f"nvfp4_32k g={g:.6g}, all 44 requests")
 
 
 def test_nvfp4_160k_and_fp8_same_batch():
     qk, w, pt, host, d = _setup("nvfp4_160k")
     data, scales = onv.quantize_fp8_rows(host, 1.0, 1.0)
     out, lse = _decode_nvfp4(qk, w, d, data, scales, 1.0)
-    b = 9
-    ro, rl = _oracle_request(w, pt, b, lambda rows: onv.dequant_nvfp4_f64(data[rows], scales[rows], 1.0))
-    _check(out[b], lse[b], ro, rl, f"nvfp4_160k b={b}")
-    out8, lse8 = qk.mla_decode_fp8(d["q"], _dev(host), 1.0, d["indptr"], d["indices"], d["lens"], w.page_size,
-                                   w.kv_len, w.sm_scale)
-    torch.cuda.synchronize()
-    ro, rl = _oracle_request(w, pt, b, lambda rows: onv.dequant_fp8_f64(host[rows], 1.0))
-    _check(out8[b].double().cpu().numpy(), lse8[b].double().cpu().numpy(), ro, rl, f"fp8 at 160k b={b}")
+    ro, rl = _oracle_all(w, pt, lambda rows: onv.dequant_nvfp4_f64(data[rows], scales[rows], 1.0))
+    _check(out, lse, ro, rl, "nvfp4_160k, all 10 requests")
+    del data, scales
+    out8, lse8 = _decode_fp8(qk, w, d, host)
+    ro, rl = _oracle_all(w, pt, lambda rows: onv.dequant_fp8_f64(host[rows], 1.0))
+    _check(out8, lse8, ro, rl, "fp8 at the 160k batch, all 10 requests")
 
 
 def test_nvfp4_1m():
@@ -101,6 +115,5 @@ def test_nvfp4_1m():
     data, scales = onv.quantize_fp8_rows(host, 1.0, 1.0)
     del host
     out, lse = _decode_nvfp4(qk, w, d, data, scales, 1.0)
-    b = 1
-    ro, rl = _oracle_request(w, pt, b, lambda rows: onv.dequant_nvfp4_f64(data[rows], scales[rows], 1.0))
-    _check(out[b], lse[b], ro, rl, f"nvfp4_1m b={b}")
+    ro, rl = _oracle_all(w, pt, lambda rows: onv.dequant_nvfp4_f64(data[rows], scales[rows], 1.0))
+    _check(out, lse, ro, rl, "nvfp4_1m, both requests")

@@ -121,3 +121,62 @@ def test_bf16_rounding_vs_torch():
     x = x[np.isfinite(x)]
     ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     np.testing.assert_array_equal(codecs.bf16_round_bits(x), ref)
+
+
+def _same_f64(a, b):
+    """Equal values with equal signs, NaN at the same positions."""
+    a, b = np.asarray(a, dtype=np.float64), np.asarray(b, dtype=np.float64)
+    na, nb = np.isnan(a), np.isnan(b)
+    np.testing.assert_array_equal(na, nb)
+    np.testing.assert_array_equal(a[~na], b[~nb])
+    np.testing.assert_array_equal(np.signbit(a[~na]), np.signbit(b[~nb]))
+
+
+def test_bf16_widening_vs_torch_every_pattern():
+    """codecs.bf16_bits_to_f64 and the C twin's bf16 rows -> fp32 widen every one of the 65,536
+    bf16 bit patterns exactly as torch's bfloat16 -> float64 / float32 casts do."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    lib = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+    _same_f64(codecs.bf16_bits_to_f64(bits), lib.to(torch.float64).numpy())
+    c32 = nvfp4.bf16_rows_to_f32(bits.reshape(-1, 64))
+    assert c32.dtype == np.float32
+    _same_f64(c32.reshape(-1), lib.to(torch.float32).numpy())
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.75, 2.0 ** -7, 3.3, 1e-30])
+def test_fp8_rows_to_f32_vs_torch_every_code(scale):
+    """The write path's FP8 source values fl32(e4m3(code) * src_scale), all 256 codes: torch's
+    float8_e4m3fn -> float32 cast times the fp32 scale in one IEEE fp32 multiply."""
+    codes = np.tile(np.arange(256, dtype=np.uint8), 3).reshape(-1, 64)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32) * torch.tensor(np.float32(scale))
+    got = nvfp4.fp8_rows_to_f32(codes, scale)
+    assert got.dtype == np.float32
+    _same_f64(got, ref.numpy())
+
+
+def test_calibrated_global_scale_rounds_the_exact_quotient():
+    """g = amax / (6 * 448) rounded once to the nearest fp32 (ties to even): hand values where the
+    quotient is exact, and random amax where the exact rational quotient is rounded here with
+    fractions (no floating-point division involved)."""
+    from fractions import Fraction
+    assert nvfp4.calibrated_global_scale(2688.0) == 1.0
+    assert nvfp4.calibrated_global_scale(5376.0) == 2.0
+    assert nvfp4.calibrated_global_scale(1344.0) == 0.5
+    assert nvfp4.calibrated_global_scale(42.0) == 2.0 ** -6          # 42 * 64 = 2688
+
+    def round_f32(q: Fraction) -> float:
+        # nearest fp32 to a positive rational q in the normal range, ties to even
+        e = q.numerator.bit_length() - q.denominator.bit_length()
+        while Fraction(2) ** e > q:
+            e -= 1
+        while Fraction(2) ** (e + 1) <= q:
+            e += 1
+        ulp = Fraction(2) ** (e - 23)
+        n, r = divmod(q, ulp)
+        if r > ulp / 2 or (r == ulp / 2 and n % 2 == 1):
+            n += 1
+        return float(n * ulp)
+    rng = np.random.default_rng(7)
+    for amax in rng.uniform(0.01, 1e4, 500).astype(np.float32):
+        want = round_f32(Fraction(float(amax)) / 2688)
+        assert nvfp4.calibrated_global_scale(float(amax)) == want, amax
