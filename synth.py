@@ -215,3 +215,23 @@ def build_fp8_pool(w: Workload, pt: PageTable, threads: int = 16) -> np.ndarray:
         list(ex.map(lambda p: pool.__setitem__(slice(int(p) * P, int(p) * P + P), filler_fp8(w, int(p))),
                     pt.free_pages))
     return pool
+
+
+def build_bf16_source_pool(w: Workload, pt: PageTable, threads: int = 16) -> np.ndarray:
+    """The requests' KV source rows rounded to bf16 (torch's cast), as uint16 bits [pool_tokens, 576],
+    at the same pool rows as build_fp8_pool; rows no request owns are zero.  For NVFP4 workloads this
+    is the bf16 tensor the FP8 rows were cast from."""
+    pool = np.zeros((w.pool_tokens, D), dtype=np.uint16)
+    P = w.page_size
+
+    def fill_chunk(task) -> None:
+        b, c0 = task
+        n = min(CHUNK, int(pt.kv_lens[b]) - c0)
+        pages = pt.kv_indices[pt.kv_indptr[b]:pt.kv_indptr[b + 1]]
+        j = np.arange(c0, c0 + n)
+        pool[pages[j // P].astype(np.int64) * P + j % P] = to_bf16_bits(kv_fp32(w, b, c0, n))
+
+    tasks = [(b, c0) for b in range(w.batch) for c0 in range(0, int(pt.kv_lens[b]), CHUNK)]
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(fill_chunk, tasks))
+    return pool
