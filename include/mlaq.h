@@ -135,6 +135,26 @@ mlaq_status mla_decode_nvfp4(const mlaq_decode_params* p, const uint16_t* q, con
                              const int32_t* kv_indices, const int32_t* kv_lens, float* out, float* lse,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Allocation-free NVFP4 decode, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same computation, kernels
+ * and arguments as mla_decode_nvfp4, without the workspace: the split partials go to a scratch
+ * array of MLAQ_NOALLOC_SCRATCH_BYTES (48 MiB) that the library holds on each device it runs on
+ * until the process ends.  The call allocates and frees nothing; its first call on a device looks
+ * the array's address up once.  The split plan is mla_decode_nvfp4's whenever its partials fit the
+ * scratch (the outputs are then bit for bit those of mla_decode_nvfp4; the pages' workloads, up to
+ * 48 requests at 32K context, 27 at 160K and 12 at 1M, all fit), else the largest split count whose
+ * partials fit (the outputs then equal mla_decode_nvfp4's with that num_splits).  A forced
+ * num_splits whose partials do not fit, or a batch whose partials do not fit even at the fewest
+ * splits the per-split token cap allows, returns MLAQ_ERR_WORKSPACE before any launch.  Every call
+ * on one device shares that device's scratch, which keeps the last call's contents (nothing in it
+ * has to start at zero): calls that overlap on one device, on different streams or from different
+ * threads, race and give wrong outputs; serialize them. */
+#define MLAQ_NOALLOC_SCRATCH_BYTES (48u << 20)
+mlaq_status mla_decode_nvfp4_noalloc(const mlaq_decode_params* p, const uint16_t* q, const uint8_t* kv_data,
+                                     const uint8_t* kv_scales, float global_scale, const int32_t* kv_indptr,
+                                     const int32_t* kv_indices, const int32_t* kv_lens, float* out, float* lse,
+                                     hipStream_t stream);
+
 /* Fused append-then-attend over an NVFP4 pool (one decode call per layer and step): token
  * kv_lens[b] - 1 of every request is the new token.  Its pool row (found through the page
  * table like any other token) is overwritten with the NVFP4 encoding of new_kv[b], exactly as

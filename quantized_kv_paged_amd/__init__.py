@@ -49,6 +49,7 @@ _SIGS = {
     "mla_decode_fp8": ([_pp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "mla_decode_nvfp4": ([_pp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "mla_decode_bf16": ([_pp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "mla_decode_nvfp4_noalloc": ([_pp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "mlaq_decode_nvfp4_append_workspace_bytes": ([_pp], _sz),
     "mla_decode_nvfp4_append": ([_pp, _vp, _vp, ctypes.c_int, _f32, _vp, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp,
                                  _sz, _vp], ctypes.c_int),
@@ -170,6 +171,18 @@ def mla_decode_nvfp4(q, kv_data, kv_scales, global_scale, kv_indptr, kv_indices,
     return out, lse
 
 
+def mla_decode_nvfp4_noalloc(q, kv_data, kv_scales, global_scale, kv_indptr, kv_indices, kv_lens, page_size,
+                             max_kv_len, sm_scale, *, num_splits=0, out=None, lse=None, want_lse=True, stream=None):
+    """mla_decode_nvfp4 without a workspace: the split partials live in the library's per-device
+    scratch (calls on one device must not overlap).  Returns (out, lse)."""
+    p = _params_for(q, page_size, max_kv_len, kv_data.shape[0], sm_scale, num_splits)
+    out, lse = _decode_outputs(q, out, lse, want_lse)
+    _check(_lib.mla_decode_nvfp4_noalloc(ctypes.byref(p), _ptr(q), _ptr(kv_data), _ptr(kv_scales), global_scale,
+                                         _ptr(kv_indptr), _ptr(kv_indices), _ptr(kv_lens), _ptr(out), _ptr(lse),
+                                         _stream(stream)))
+    return out, lse
+
+
 def mla_decode_nvfp4_append(q, new_kv, new_kv_format, src_scale, kv_data, kv_scales, global_scale, kv_indptr,
                             kv_indices, kv_lens, page_size, max_kv_len, sm_scale, *, num_splits=0, out=None,
                             lse=None, want_lse=True, workspace=None, stream=None):
@@ -264,7 +277,7 @@ def read_probe(buf, num_blocks=2048, partials=None, stream=None):
     return partials
 
 
-__all__ = ["mla_decode_fp8", "mla_decode_nvfp4", "mla_decode_nvfp4_append", "mla_decode_bf16", "mla_extend_nvfp4",
+__all__ = ["mla_decode_fp8", "mla_decode_nvfp4", "mla_decode_nvfp4_noalloc", "mla_decode_nvfp4_append", "mla_decode_bf16", "mla_extend_nvfp4",
            "extend_params", "mlaq_extend_workspace_bytes", "kv_quantize_nvfp4", "kv_dequantize",
            "mlaq_decode_num_splits", "mlaq_decode_workspace_bytes", "decode_params", "alloc_workspace",
            "read_probe", "MlaqError", "version", "last_error", "EXPORTS", "LIB_PATH"]

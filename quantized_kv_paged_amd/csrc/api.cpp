@@ -299,6 +299,38 @@ mlaq_status mla_decode_nvfp4(const mlaq_decode_params* p, const uint16_t* q, con
                        out, lse, workspace, workspace_bytes, stream);
 }
 
+mlaq_status mla_decode_nvfp4_noalloc(const mlaq_decode_params* p, const uint16_t* q, const uint8_t* kv_data,
+                                     const uint8_t* kv_scales, float global_scale, const int32_t* kv_indptr,
+                                     const int32_t* kv_indices, const int32_t* kv_lens, float* out, float* lse,
+                                     hipStream_t stream) {
+  mlaq_status st = check_params(p);
+  if (st != MLAQ_OK) return st;
+  if (p->batch == 0) return MLAQ_OK;
+  const size_t cap = MLAQ_NOALLOC_SCRATCH_BYTES;
+  mlaq_decode_params plan = *p;
+  plan.num_splits = resolve_splits(mlaq::FMT_NVFP4, p);
+  if (workspace_for(p, plan.num_splits) > cap) {
+    // the automatic plan's partials do not fit: the largest split count whose partials do, if the
+    // per-split token cap allows it; a forced count is the caller's and is rejected
+    const size_t per_split = workspace_for(p, 2) / 2;   // one split's partials for the whole batch
+    int fit = (int)std::min<size_t>(cap / per_split, (size_t)MLAQ_MAX_SPLITS);
+    if (fit < 2) fit = 1;   // a single split writes the outputs directly and needs no partials
+    if (p->num_splits > 0 || fit < min_splits(p->max_kv_len))
+      return fail(MLAQ_ERR_WORKSPACE,
+                  "noalloc decode: %d splits x batch %d x %d heads need %zu bytes of partials, the scratch holds %zu",
+                  plan.num_splits, p->batch, p->num_heads, workspace_for(p, plan.num_splits), cap);
+    plan.num_splits = fit;
+  }
+  const size_t need = workspace_for(&plan, plan.num_splits);
+  void* scratch = nullptr;
+  if (need > 0) {
+    const hipError_t e = mlaq::noalloc_scratch(&scratch);
+    if (e != hipSuccess) return fail(MLAQ_ERR_LAUNCH, "noalloc decode: scratch lookup failed: %s", hipGetErrorString(e));
+  }
+  return decode_common(mlaq::FMT_NVFP4, &plan, q, kv_data, kv_scales, global_scale, kv_indptr, kv_indices, kv_lens,
+                       out, lse, scratch, scratch ? cap : 0, stream);
+}
+
 size_t mlaq_decode_nvfp4_append_workspace_bytes(const mlaq_decode_params* p) {
   if (check_params(p) != MLAQ_OK) return SIZE_MAX;
   return workspace_for(p, resolve_splits(mlaq::FMT_NVFP4, p), true);

@@ -41,6 +41,9 @@
 //     (bf16 queries are converted to fp16 exactly) fold into the score and output scales.
 #include <hip/hip_ext.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "device_common.h"
 #include "mlaq.h"
 #include "mlaq_kernels.h"
@@ -890,6 +893,36 @@ hipError_t launch_decode(int fmt, const DecodeArgs& a, hipStream_t stream, const
     case FMT_NVFP4: return launch_pages<FMT_NVFP4>(a, stream, ev);
     default: return launch_pages<FMT_BF16>(a, stream, ev);
   }
+}
+
+// ---- Scratch of the allocation-free decode (mla_decode_nvfp4_noalloc): the split partials of
+//      one call, in a file-scope device array that the code object brings with it, so the call
+//      needs no allocation.  Host code never passes the array's name to a kernel (in host code
+//      it is only a stand-in for the symbol): its device address is looked up once per device,
+//      with that device current, and kept.  Every call on a device shares that device's array.
+static __device__ __align__(256) char scratch[MLAQ_NOALLOC_SCRATCH_BYTES];
+
+hipError_t noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> addr[kMaxDevices];
+  static std::mutex mu;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(mu);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!p) return hipErrorInvalidSymbol;
+      addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 }  // namespace mlaq

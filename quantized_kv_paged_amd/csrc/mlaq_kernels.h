@@ -49,6 +49,9 @@ struct ProfileEvents {
   hipEvent_t split_start = nullptr, split_end = nullptr, merge_start = nullptr, merge_end = nullptr;
 };
 hipError_t launch_decode(int fmt, const DecodeArgs& a, hipStream_t stream, const ProfileEvents& ev);
+// device address of the allocation-free decode's scratch on the current device (looked up once
+// per device)
+hipError_t noalloc_scratch(void** ptr);
 
 struct QuantArgs {
   const void* src;            // FP8 bytes or bf16 bits [n, 576]

@@ -78,7 +78,7 @@ _BOUNDARY = {
 _ADDED = {"mlaq_decode_format_workspace_bytes", "mlaq_decode_num_splits", "mla_decode_nvfp4_append",
           "mlaq_decode_nvfp4_append_workspace_bytes", "mla_extend_nvfp4", "mlaq_extend_workspace_bytes",
           "mlaq_extend_num_splits", "mlaq_set_profile_events", "mlaq_read_probe", "mlaq_version",
-          "mla_decode_nvfp4_noalloc", "mlaq_noalloc_max_bytes"}
+          "mla_decode_nvfp4_noalloc"}
 
 
 def test_boundary_signatures():
@@ -372,3 +372,18 @@ def test_oracle_shares_nothing_with_the_hip_path():
             text = open(os.path.join(odir, f)).read()
             assert not re.search(r"import\s+quantized_kv_paged_amd|from\s+quantized_kv_paged_amd|libmlaq|csrc/|mlaq\.h",
                                  text), f
+
+
+def test_noalloc_validation():
+    """The allocation-free decode rejects, before any launch or device query, what the workspace call
+    rejects and plans whose partials do not fit its 48 MiB scratch."""
+    L = qk._lib
+
+    def na(p, q=FAKE, data=FAKE, scales=FAKE, g=1.0):
+        return L.mla_decode_nvfp4_noalloc(ctypes.byref(p), q, data, scales, g, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert na(_p(num_heads=24)) == ERR_SHAPE
+    assert na(_p(max_kv_len=65536, num_splits=1)) == ERR_SHAPE          # per-split token cap
+    assert na(_p(batch=4, max_kv_len=32768, num_splits=512)) == ERR_WORKSPACE   # forced: 4 x 512 slots
+    assert "scratch" in qk.last_error()
+    assert na(_p(batch=2000, max_kv_len=1 << 20)) == ERR_WORKSPACE      # 64 splits at least: 4.2 GB
+    assert na(_p(batch=0)) == 0
