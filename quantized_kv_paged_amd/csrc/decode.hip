@@ -73,13 +73,17 @@ constexpr float kSlack = 8.0f;          // lazy-rescale threshold of the running
 // The lane's share of one token row for its dim half dh and lane group g, as 9 k-blocks of 8
 // dims (any order of the 576 dims gives the same dot product; the query operand uses the same
 // map).  The map is chosen per format so that a lane's k-blocks are 16 contiguous bytes of
-// the row and the four lane groups of a token read 64 contiguous bytes:
-//   FP8, BF16: kb < 8 (m = kb/2, h = kb%2): value dims 256dh + 64m + 16g + 8h .. +8
-//   NVFP4:     kb < 8 (c = kb/4, s = kb%4): value dims 256dh + 128c + 32g + 8s .. +8
+// the row:
+//   FP8, BF16: kb < 8 (m = kb/2, h = kb%2): value dims 256dh + 64m + 16g + 8h .. +8 (the
+//              four lane groups of a token read 64 contiguous bytes per load)
+//   NVFP4:     kb < 8 (c = kb/4, s = kb%4): value dims 256dh + 64g + 32c + 8s .. +8 (a lane
+//              reads 32 contiguous bytes = 64 dims = four whole 16-value scale blocks, so its
+//              block scales are one aligned 4-byte word of the scale row)
 //   kb = 8: rope dims 512 + 32dh + 8g .. +8.
 template <int FMT> struct RawTile;
 template <> struct RawTile<FMT_FP8> { u32x4 d[4]; u32x2 e; };                  // 4 x 16 B + 8 B
-template <> struct RawTile<FMT_NVFP4> { u32x4 d[2]; uint32_t e; uint32_t s[5]; };  // codes + scales
+// codes (2 x 16 B + 4 B rope), the scales of blocks 16dh + 4g .. +3 (s) and rope blocks 32..35 (sr)
+template <> struct RawTile<FMT_NVFP4> { u32x4 d[2]; uint32_t e; uint32_t s; uint32_t sr; };
 template <> struct RawTile<FMT_BF16> { u32x4 d[9]; };                           // 9 x 16 B
 
 template <int FMT> struct OpType { typedef f16x8 type; typedef _Float16 elem; };
@@ -97,7 +101,7 @@ __device__ __forceinline__ int vswz(int r) { const int x = r & 15; return (x ^ (
 template <int FMT>
 __device__ __forceinline__ int kb_dim(int dh, int kb, int g) {
   if (kb == 8) return 512 + 32 * dh + 8 * g;
-  return FMT == FMT_NVFP4 ? 256 * dh + 128 * (kb >> 2) + 32 * g + 8 * (kb & 3)
+  return FMT == FMT_NVFP4 ? 256 * dh + 64 * g + 32 * (kb >> 2) + 8 * (kb & 3)
                           : 256 * dh + 64 * (kb >> 1) + 16 * g + 8 * (kb & 1);
 }
 
@@ -153,12 +157,11 @@ __device__ __forceinline__ void load_raw(RawTile<FMT>& r, const DecodeArgs& a, i
   } else if constexpr (FMT == FMT_NVFP4) {
     const uint8_t* base = a.kv + row * kNvData;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) r.d[c] = *reinterpret_cast<const u32x4*>(base + 128 * dh + 64 * c + 16 * g);
+    for (int c = 0; c < 2; ++c) r.d[c] = *reinterpret_cast<const u32x4*>(base + 128 * dh + 32 * g + 16 * c);
     r.e = *reinterpret_cast<const uint32_t*>(base + 256 + 16 * dh + 4 * g);
     const uint32_t* sp = reinterpret_cast<const uint32_t*>(a.kv_scales + row * kNvScale);
-    const u32x4 s4 = *reinterpret_cast<const u32x4_a4*>(sp + 4 * dh);   // blocks 16dh .. 16dh+15
-    r.s[0] = s4[0]; r.s[1] = s4[1]; r.s[2] = s4[2]; r.s[3] = s4[3];
-    r.s[4] = sp[8];                                                      // rope blocks 32 .. 35
+    r.s = sp[4 * dh + g];   // blocks 16dh + 4g .. +3
+    r.sr = sp[8];           // rope blocks 32 .. 35
   } else {
     const uint16_t* base = reinterpret_cast<const uint16_t*>(a.kv) + row * kD;
 #pragma unroll
@@ -173,7 +176,7 @@ __device__ __forceinline__ void load_raw(RawTile<FMT>& r, const DecodeArgs& a, i
 // Same loads for a tile whose rows are contiguous in the pool: buffer loads through
 // descriptors whose base is the tile's first row (kv, and the NVFP4 scales in sc) and whose
 // size covers only the tile's valid rows, so the lanes of other rows read zeros; the lane's
-// constant byte offsets are o.v (value part), o.e (rope part), o.s (NVFP4 scales, row share).
+// constant byte offsets are o.v (value part), o.e (rope part), o.s (NVFP4 scale row).
 struct LaneOffsets { uint32_t v, e, s; };
 template <int FMT>
 __device__ __forceinline__ LaneOffsets lane_offsets(int tok_in_tile, int dh, int g) {
@@ -183,9 +186,9 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int tok_in_tile, int dh, int
     o.e = tok_in_tile * kD + 512 + 32 * dh + 8 * g;
     o.s = 0;
   } else if constexpr (FMT == FMT_NVFP4) {
-    o.v = tok_in_tile * kNvData + 128 * dh + 16 * g;
+    o.v = tok_in_tile * kNvData + 128 * dh + 32 * g;
     o.e = tok_in_tile * kNvData + 256 + 16 * dh + 4 * g;
-    o.s = tok_in_tile * kNvScale + 16 * dh;
+    o.s = tok_in_tile * kNvScale;
   } else {
     o.v = 2 * (tok_in_tile * kD + 256 * dh + 16 * g);
     o.e = 2 * (tok_in_tile * kD + 512 + 32 * dh + 8 * g);
@@ -196,7 +199,7 @@ __device__ __forceinline__ LaneOffsets lane_offsets(int tok_in_tile, int dh, int
 
 template <int FMT>
 __device__ __forceinline__ void load_raw_tile(RawTile<FMT>& r, BufferRsrc kv, BufferRsrc sc, const LaneOffsets& o,
-                                              int dh, int tok0) {
+                                              int dh, int g, int tok0) {
   if constexpr (FMT == FMT_FP8) {
     const uint32_t so = tok0 * kD;
 #pragma unroll
@@ -205,11 +208,10 @@ __device__ __forceinline__ void load_raw_tile(RawTile<FMT>& r, BufferRsrc kv, Bu
   } else if constexpr (FMT == FMT_NVFP4) {
     const uint32_t so = tok0 * kNvData, ss = tok0 * kNvScale;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) r.d[c] = buffer_load_b128(kv, o.v + 64 * c, so);
+    for (int c = 0; c < 2; ++c) r.d[c] = buffer_load_b128(kv, o.v + 16 * c, so);
     r.e = buffer_load_b32(kv, o.e, so);
-    const u32x4 s4 = buffer_load_b128(sc, o.s, ss);          // blocks 16dh .. 16dh+15
-    r.s[0] = s4[0]; r.s[1] = s4[1]; r.s[2] = s4[2]; r.s[3] = s4[3];
-    r.s[4] = buffer_load_b32(sc, o.s - 16 * dh + 32, ss);    // rope blocks 32 .. 35
+    r.s = buffer_load_b32(sc, o.s + 16 * dh + 4 * g, ss);    // blocks 16dh + 4g .. +3
+    r.sr = buffer_load_b32(sc, o.s + 32, ss);                // rope blocks 32 .. 35
   } else {
     const uint32_t so = tok0 * 2 * kD;
 #pragma unroll
@@ -239,8 +241,8 @@ __device__ __forceinline__ void fix_raw(RawTile<FMT>& r, int state) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) r.d[c][e] = state ? 0u : r.d[c][e];
     r.e = state ? 0u : r.e;
-#pragma unroll
-    for (int k = 0; k < 5; ++k) r.s[k] = state ? f : r.s[k];
+    r.s = state ? f : r.s;
+    r.sr = state ? f : r.sr;
   } else {
     const uint32_t f = state == 2 ? 0x7fc07fc0u : 0u;
 #pragma unroll
@@ -250,12 +252,12 @@ __device__ __forceinline__ void fix_raw(RawTile<FMT>& r, int state) {
   }
 }
 
-// MFMA operand of k-block KB of the lane's row half.  NVFP4: the 16-dim blocks of k-blocks
-// 4c + s are bytes 2g (s < 2) and 2g + 1 (s >= 2) of the dword pair (s[2c], s[2c + 1]);
-// selector ssel[0] picks both, each replicated into the two halves of an fp16 pair; the
-// block of k-block 8 is byte 2dh + g/2 of s[4] (selector ssel[1]).
+// MFMA operand of k-block KB of the lane's row half.  NVFP4: the 16-dim block of k-block
+// 4c + s is byte 2c + s/2 of s; one byte permutation gives bytes (2c, 2c, 2c + 1, 2c + 1), whose
+// low or high pair converts to that block's scale in both halves of an fp16 pair; the block of
+// k-block 8 is byte 2dh + g/2 of sr (selector ssel).
 template <int FMT, int KB>
-__device__ __forceinline__ typename OpType<FMT>::type dequant(const RawTile<FMT>& r, const uint32_t* ssel) {
+__device__ __forceinline__ typename OpType<FMT>::type dequant(const RawTile<FMT>& r, uint32_t ssel) {
   if constexpr (FMT == FMT_FP8) {
     const uint32_t w0 = KB < 8 ? r.d[KB >> 1][2 * (KB & 1)] : r.e[0];
     const uint32_t w1 = KB < 8 ? r.d[KB >> 1][2 * (KB & 1) + 1] : r.e[1];
@@ -265,10 +267,10 @@ __device__ __forceinline__ typename OpType<FMT>::type dequant(const RawTile<FMT>
   } else if constexpr (FMT == FMT_NVFP4) {
     f16x2 s2;
     if constexpr (KB < 8) {
-      const uint32_t sb = __builtin_amdgcn_perm(r.s[2 * (KB >> 2) + 1], r.s[2 * (KB >> 2)], ssel[0]);
+      const uint32_t sb = __builtin_amdgcn_perm(r.s, r.s, (KB >> 2) ? 0x03030202u : 0x01010000u);
       s2 = fp8x2_to_f16<((KB & 3) >= 2)>(sb);
     } else {
-      s2 = fp8x2_to_f16<false>(__builtin_amdgcn_perm(0u, r.s[4], ssel[1]));
+      s2 = fp8x2_to_f16<false>(__builtin_amdgcn_perm(0u, r.sr, ssel));
     }
     const uint32_t w = KB < 8 ? r.d[KB >> 2][KB & 3] : r.e;
     const f16x2 a = fp4x2_to_f16<0>(w) * s2, b = fp4x2_to_f16<1>(w) * s2;
@@ -400,8 +402,9 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
     return;
   }
 
-  // ---- running state of this wave's stream: m, l for head l16; O for heads 4grp+i,
-  //      dims 256dh + 16nt + l16
+  // ---- running state of this wave's stream: m for head l16, l_run the sum of the lane's own
+  //      probabilities of head l16 (the lane groups' sums are added at the end of the chunk);
+  //      O for heads 4grp+i, dims 256dh + 16nt + l16
   float m_run = kMinusBig, l_run = 0.0f;
   f32x4 o[16];
 #pragma unroll
@@ -412,7 +415,7 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
   char* const vt = smem + w * kWaveV;
   float* const sX = reinterpret_cast<float*>(smem + kSwap);
   // one raw tile per wave: refilled with the next tile's rows as soon as it is converted (two
-  // in flight did not fit the registers next to the output accumulator)
+  // in flight do not fit the registers next to the output accumulator)
   RawTile<FMT> rawA[kBlocks];
   int stA[kBlocks];
   // prologue, ordered for the in-order load counter: the first two page-table batches, this
@@ -441,7 +444,7 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
       for (int tb = 0; tb < kBlocks; ++tb) {
         const int tt = my_tok + 16 * tb;
         s[tb] = t0 + tt >= t_end ? 1 : (tt >= nvalid ? 2 : 0);
-        load_raw_tile<FMT>(r[tb], kv, sc, lofs, dh, 16 * tb);
+        load_raw_tile<FMT>(r[tb], kv, sc, lofs, dh, grp, 16 * tb);
       }
     } else {
 #pragma unroll
@@ -495,22 +498,22 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
     }
   }
 
-  // NVFP4 block-scale byte selectors (see dequant)
-  uint32_t ssel[2];
+  // NVFP4 rope block-scale byte selector (see dequant)
+  uint32_t ssel;
   {
-    const uint32_t b0 = 2u * grp, b1 = (uint32_t)(2 * dh + (grp >> 1));
-    ssel[0] = b0 | (b0 << 8) | ((b0 + 1) << 16) | ((b0 + 1) << 24);
-    ssel[1] = b1 | (b1 << 8) | 0x0c0c0000u;
+    const uint32_t b1 = (uint32_t)(2 * dh + (grp >> 1));
+    ssel = b1 | (b1 << 8) | 0x0c0c0000u;
   }
   // Byte addresses in the wave's value tile (rows = its 32 tokens 16tb + r, dims relative to
   // 256dh).  Writes of k-block kb of block tb: row 16tb + l16, chunk kb_dim / 8 stored at its
   // bits 0-3 XOR vswz(l16): FP8 / BF16 chunk 16(m >> 1) + (8(m & 1) | 2g | h) for kb = 2m + h,
-  // i.e. vwb ^ 16(8(m & 1) | h), plus 256(m >> 1); NVFP4 chunk 16c + (4g | s) for kb = 4c + s,
-  // i.e. vwb ^ 16s, plus 256c; plus 16 kVRow tb.  (Both write patterns and the reads below are
+  // i.e. vwb ^ 16(8(m & 1) | h), plus 256(m >> 1); NVFP4 chunk 16(g >> 1) + (8(g & 1) | kb),
+  // i.e. vwb ^ 16kb; plus 16 kVRow tb.  (Both write patterns and the reads below are
   // conflict-free, checked by enumeration.)  Transposed reads of dims 16nt + 4q .. +3 of block tb by lane
   // (g, 4i + q): row 16tb + 4g + i, chunk 16(nt >> 3) + ((2(nt & 7) | (q >> 1)) ^ vswz(row)),
   // i.e. vrb ^ 32(nt & 7), plus 256(nt >> 3) + 16 kVRow tb.
-  const int vwb = l16 * kVRow + 16 * (((FMT == FMT_NVFP4 ? 4 : 2) * grp) ^ vswz(l16));
+  const int vwb = FMT == FMT_NVFP4 ? l16 * kVRow + 256 * (grp >> 1) + 16 * ((8 * (grp & 1)) ^ vswz(l16))
+                                   : l16 * kVRow + 16 * ((2 * grp) ^ vswz(l16));
   const int q4 = l16 & 3, vrow = 4 * grp + (l16 >> 2);
   const int vrb = vrow * kVRow + 16 * ((q4 >> 1) ^ vswz(vrow)) + 8 * (q4 & 1);
 
@@ -530,8 +533,9 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
       const Op kop = dequant<FMT, KB>(cur[tb], ssel);                                             \
       sacc[tb] = mfma16x16x32(kop, qop[KB], sacc[tb]);                                            \
       if (KB < 8)                                                                                 \
-        *reinterpret_cast<Op*>(vt + ((vwb ^ (16 * (FMT == FMT_NVFP4 ? (KB & 3) : (KB & 2) * 4 + (KB & 1)))) + \
-                                     256 * (KB >> 2) + 16 * kVRow * tb)) = kop;                   \
+        *reinterpret_cast<Op*>(vt + (FMT == FMT_NVFP4 ? (vwb ^ (16 * KB))                         \
+                                     : (vwb ^ (16 * ((KB & 2) * 4 + (KB & 1)))) + 256 * (KB >> 2)) + \
+                                     16 * kVRow * tb) = kop;                                     \
     }
     MLAQ_QK_STEP(0) MLAQ_QK_STEP(1) MLAQ_QK_STEP(2) MLAQ_QK_STEP(3) MLAQ_QK_STEP(4)
     MLAQ_QK_STEP(5) MLAQ_QK_STEP(6) MLAQ_QK_STEP(7) MLAQ_QK_STEP(8)
@@ -593,13 +597,15 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
       for (int i = 0; i < 4; ++i) sc[4 * tb + i] = sp[tb][i] + sq[tb][i];
     // The reference point m_run of the exponentials moves only when a score exceeds it by more
     // than kSlack (log2 units), so probabilities stay below 2^kSlack (exact in fp16 / bf16 and
-    // far from overflow in the fp32 sums) and the accumulators are rescaled only then.
+    // far from overflow in the fp32 sums) and the accumulators are rescaled only then.  Whether
+    // any head must move is one vote over the lanes' own maxima; the heads' maxima over their
+    // lane groups are formed only then.
     float lmax = sc[0];
 #pragma unroll
     for (int j = 1; j < 4 * kBlocks; ++j) lmax = fmaxf(lmax, sc[j]);
-    const float tmax = rows_max(lmax);
-    const bool grow = tmax > m_run + kSlack;
-    if (__any(grow)) {
+    if (__any(lmax > m_run + kSlack)) {
+      const float tmax = rows_max(lmax);
+      const bool grow = tmax > m_run + kSlack;
       const float m_new = grow ? tmax : m_run;
       const float alpha = fast_exp2(m_run - m_new);
       l_run *= alpha;
@@ -630,7 +636,7 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
       else
         rsum = __builtin_amdgcn_fdot2(f16x2{pop[j], pop[j + 1]}, f16x2{(_Float16)1.0f, (_Float16)1.0f}, rsum, false);
     }
-    l_run += rows_sum(rsum);
+    l_run += rsum;
     // O += P V: 16 dims per product, K = this group's 32 tokens.  The operands are read in
     // batches of kVAhead dim blocks, each batch issued before the products of the previous
     // one (scheduling barriers keep the compiler from shortening that distance, so a product
@@ -652,6 +658,7 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
   // ---- tile loop; the score swap buffers alternate with the tiles
   for (int k = 0; k < ntiles; ++k) compute(rawA, stA, t_begin + k * kTile, k & 1, k + 1 < ntiles);
 
+  l_run = rows_sum(l_run);   // head l16's sum over the stream's tokens, in every lane group
   // ---- end of the chunk: merge of the token-group streams.  Stream tg: running max m_tg, sum
   //      l_tg; weights w_tg = 2^(m_tg - M), M = max_tg m_tg; L = sum_tg w_tg l_tg.
   //      Each wave leaves its accumulator in its own value tile, which no other wave reads and
