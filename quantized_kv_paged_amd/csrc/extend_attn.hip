@@ -76,7 +76,8 @@ __global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArg
   u32x4 raw[3];
   auto load = [&](int tt) __attribute__((always_inline)) {
     const int r0 = tt * kXRows;
-    const int nrows = max(0, min(kXRows, rows_blk - r0));
+    // uniform, and kept in a scalar register so the descriptor is one too (no per-lane loop)
+    const int nrows = __builtin_amdgcn_readfirstlane(max(0, min(kXRows, rows_blk - r0)));
     const BufferRsrc rs = make_rsrc(reg + (int64_t)r0 * kD, nrows * kD);
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
@@ -147,6 +148,7 @@ __global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArg
   const int q4 = l16 & 3, vrow = 4 * grp + (l16 >> 2);
   const int vrb = vrow * kXRowB + 16 * ((q4 >> 1) ^ xswz(vrow)) + 8 * (q4 & 1) + 512 * dh;
 
+  // m for head l16; l_run the sum of the lane's own probabilities of head l16
   float m_run = kXMinusBig, l_run = 0.0f;
   f32x4 o[16];
 #pragma unroll
@@ -200,12 +202,14 @@ __global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArg
 #pragma unroll
       for (int j = 0; j < 4; ++j) sc[4 * tb + j] = sp[tb][j] + sq[j];
     }
+    // lazy rescale as in the decode kernel: one vote over the lanes' own maxima, the heads'
+    // maxima over their lane groups only when some reference must move
     float lmax = sc[0];
 #pragma unroll
     for (int j = 1; j < 8; ++j) lmax = fmaxf(lmax, sc[j]);
-    const float tmax = rows_max(lmax);
-    const bool grow = tmax > m_run + kXSlack;
-    if (__any(grow)) {
+    if (__any(lmax > m_run + kXSlack)) {
+      const float tmax = rows_max(lmax);
+      const bool grow = tmax > m_run + kXSlack;
       const float m_new = grow ? tmax : m_run;
       const float alpha = fast_exp2(m_run - m_new);
       l_run *= alpha;
@@ -226,7 +230,7 @@ __global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArg
 #pragma unroll
     for (int j = 0; j < 8; j += 2)                 // the rounded probabilities the products use
       rsum = __builtin_amdgcn_fdot2(f16x2{pop[j], pop[j + 1]}, f16x2{(_Float16)1.0f, (_Float16)1.0f}, rsum, false);
-    l_run += rows_sum(rsum);
+    l_run += rsum;   // the lane's own rows; lane groups are added after the last tile
 #pragma unroll
     for (int nt = 0; nt < 16; ++nt) {
       const char* pv = tile + ((vrb ^ (32 * (nt & 7))) + 256 * (nt >> 3));
@@ -237,6 +241,7 @@ __global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArg
   }
 
   // ---- outputs of this token: O for heads 4g + i, dims 256dh + 16nt + l16; (m, l) for head l16
+  l_run = rows_sum(l_run);
   if (!tok) return;
   if (a.num_splits == 1) {
 #pragma unroll
