@@ -22,6 +22,7 @@ Prints ONE JSON line.  `value` = KV bytes read per step / measured time per step
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import ctypes
 import hashlib
 import json
@@ -355,6 +356,31 @@ def decode_config(bn, w, primary, headline=False, extras=True):
     return res, ctx
 
 
+def split_sweep(bn, w, fmt, counts):
+    """The workload's decode step (without the write path) in one format at forced split counts:
+    one JSON line per count with the step, split-kernel and merge times (the planner's choice is
+    marked).  A measurement aid for the split planner; not part of the benchmark line."""
+    torch, qk = bn.torch, bn.qk
+    pt, host, d = bn.inputs(w)
+    fp8_dev = bn.dev(host)
+    kv_bytes = w.batch * w.kv_len * ROW_BYTES[fmt]
+    n = bn.layers_for(kv_bytes)
+    layers = [fp8_dev] + [fp8_dev.clone() for _ in range(n - 1)] if fmt == "fp8" else bn.nvfp4_layers(fp8_dev, n)
+    out = torch.empty((w.batch, w.heads, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.batch, w.heads), dtype=torch.float32, device="cuda")
+    fcode = qk.MLAQ_FP8_E4M3 if fmt == "fp8" else qk.MLAQ_NVFP4
+    planned = qk.mlaq_decode_num_splits(qk.decode_params(w.batch, w.heads, w.page_size, w.kv_len,
+                                                         w.pool_tokens, w.sm_scale), fcode)
+    for c in counts:
+        p = qk.decode_params(w.batch, w.heads, w.page_size, w.kv_len, w.pool_tokens, w.sm_scale, num_splits=c)
+        ws = torch.zeros(max(qk.mlaq_decode_workspace_bytes(p, fcode), 256), dtype=torch.uint8, device="cuda")
+        t = bn.timed(bn.decode_step(fmt, p, d, layers, out, lse, ws), n)
+        line = {"sweep": w.name, "kv_format": fmt, "batch": w.batch, "kv_len": w.kv_len, "planned": c == planned,
+                **summary(t, kv_bytes, c)}
+        print(json.dumps(line), flush=True)
+        del ws
+
+
 def write_path_leg(bn, w, ctx):
     """The quantize-on-write of the workload's write chunk on its own (FP8 source -> NVFP4 rows in
     scattered pages): microseconds per call, tokens/s and GB/s of algorithmic bytes (source read,
@@ -592,6 +618,14 @@ def main():
                     help="untimed steps first (clocks and memory settle over the first tens of ms)")
     ap.add_argument("--workload", default="nvfp4_1m", choices=WORKLOADS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--split-sweep", default=None,
+                    help="comma-separated split counts: time the workload's decode at each (one JSON line "
+                         "per count) instead of the benchmark line")
+    ap.add_argument("--sweep-format", default=None, choices=("fp8", "nvfp4"),
+                    help="the format of --split-sweep (default: the workload's own)")
+    ap.add_argument("--sweep-shape", default=None,
+                    help="BATCH:CONTEXT for --split-sweep: the workload's distributions and page size at "
+                         "another batch and context (pool = batch x context)")
     ap.add_argument("--no-extras", action="store_true", help="the headline workload's own format only")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
@@ -604,6 +638,13 @@ def main():
     bn = Bench(args.steps, args.warmup)
     torch = bn.torch
     w = synth.WORKLOADS[args.workload]
+    if args.split_sweep:
+        if args.sweep_shape:
+            sb, sl = (int(x) for x in args.sweep_shape.split(":"))
+            w = dataclasses.replace(w, name=f"{w.name}@{sb}x{sl}", batch=sb, kv_len=sl, pool_tokens=sb * sl,
+                                    write_tokens=0, write_pages=0)
+        split_sweep(bn, w, args.sweep_format or w.fmt, [int(x) for x in args.split_sweep.split(",")])
+        return
     extras = not args.no_extras
     # the read probe first: it is reported, and it brings the clocks up before any timed region
     probe = read_probe(bn) if extras else None

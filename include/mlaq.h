@@ -142,7 +142,7 @@ mlaq_status mla_decode_nvfp4(const mlaq_decode_params* p, const uint16_t* q, con
  * until the process ends.  The call allocates and frees nothing; its first call on a device looks
  * the array's address up once.  The split plan is mla_decode_nvfp4's whenever its partials fit the
  * scratch (the outputs are then bit for bit those of mla_decode_nvfp4; the pages' workloads, up to
- * 48 requests at 32K context, 27 at 160K and 12 at 1M, all fit), else the largest split count whose
+ * 128 requests at 32K context, 56 at 160K and 16 at 1M, all fit), else the largest split count whose
  * partials fit (the outputs then equal mla_decode_nvfp4's with that num_splits).  A forced
  * num_splits whose partials do not fit, or a batch whose partials do not fit even at the fewest
  * splits the per-split token cap allows, returns MLAQ_ERR_WORKSPACE before any launch.  Every call

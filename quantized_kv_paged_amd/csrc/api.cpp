@@ -37,16 +37,32 @@ int min_splits(int64_t max_kv_len) {
 
 // Split planning.  Every workgroup processes one (request, chunk, 16-head group) in tiles of
 // the format's tile size; with all requests at the host-known bound, workgroups run in
-// "rounds" of the resident slots (CUs x workgroups per CU).  The cost (in tile-times) is
-// rounds * (tiles per chunk + fixed per-workgroup cost) plus the partial write + merge read,
-// and the smallest-cost split count is taken (ties -> fewer splits).
+// "rounds" of the resident slots (CUs x workgroups per CU).  Costs are in tile-times, the time
+// a workgroup takes for one tile when every slot is busy:
+//   rounds * (tiles per chunk + fixed)       each workgroup streams its chunk and pays a
+//                                           prologue / epilogue (page ids, first tile, stream
+//                                           merge) of about one tile;
+//   + crowd * (workgroups on the fullest CU) those fixed latencies grow with the workgroups that
+//                                           share a CU (about 3 us each), which is why a small
+//                                           batch runs faster on fewer, longer chunks;
+//   + rounds * part + part * wgs / slots     with several splits, each workgroup writes a partial
+//   + merge                                 and the merge kernel reads them all (its launch
+//                                           about one tile-time);
+// where part is a partial's bytes (16 heads x 512 fp32 + 32 fp32 = 32,896 B) over a tile's KV
+// bytes: 3.2 tiles for NVFP4 (32 tokens x 324 B), 0.89 for FP8 (64 x 576 B), 0.45 for BF16 (64 x
+// 1,152 B).  The smallest cost is taken (ties -> fewer splits).  The constants are fitted to
+// forced-split sweeps at 12 shapes (32K to 1M tokens per request, 1 to 44 requests, both
+// formats); the plan is the fastest measured split count at 11 of them and within 3 % at the
+// other.
 int plan_splits(int fmt, int batch, int head_groups, int max_kv_len) {
   const int streams = mlaq::decode_streams(fmt);
   const int tile = mlaq::decode_tile(streams);
   const double slots = (double)mlaq::kComputeUnits * mlaq::decode_groups_per_cu(streams);
   const int tiles = (max_kv_len + tile - 1) / tile;
   if (tiles <= 1 || batch <= 0) return 1;
-  const double fixed = 0.5, merge = 0.5;
+  const double row_bytes = fmt == mlaq::FMT_NVFP4 ? 324.0 : fmt == mlaq::FMT_FP8 ? 576.0 : 1152.0;
+  const double part = (16.0 * 512.0 * 4.0 + 32.0 * 4.0) / (tile * row_bytes);
+  const double fixed = 1.2, crowd = 1.25, merge = 1.0;
   const int smin = min_splits(max_kv_len);
   int best = smin;
   double best_cost = std::numeric_limits<double>::infinity();
@@ -55,7 +71,8 @@ int plan_splits(int fmt, int batch, int head_groups, int max_kv_len) {
     const double wgs = (double)batch * head_groups * s;
     const double rounds = std::ceil(wgs / slots);
     const double per = std::ceil((double)tiles / s);
-    const double cost = rounds * (per + fixed) + (s > 1 ? merge * wgs / slots : 0.0);
+    double cost = rounds * (per + fixed) + crowd * std::ceil(std::min(wgs, slots) / mlaq::kComputeUnits);
+    if (s > 1) cost += rounds * part + part * wgs / slots + merge;
     if (cost < best_cost - 1e-9) { best_cost = cost; best = s; }
   }
   return best;

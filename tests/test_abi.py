@@ -240,6 +240,21 @@ def test_split_planning_and_workspace():
         qk.mlaq_decode_workspace_bytes(_p(num_heads=20))
 
 
+def test_split_planning_follows_the_measured_sweep():
+    # forced-split sweeps of the decode step (split kernel + merge) on MI355X, recorded in
+    # profiles/mla_decode_kernel_split_counts.md: the fastest count at each shape (at 16 x 4K the
+    # plan's 32 was 3 % behind 43).  Small batches run fastest on one workgroup per CU with a few
+    # tiles each, large ones on every slot filled once.
+    fastest = {("nvfp4", 8, 32768): 128, ("nvfp4", 44, 32768): 23, ("nvfp4", 10, 163840): 101,
+               ("nvfp4", 2, 1048576): 512, ("fp8", 8, 32768): 64, ("fp8", 2, 1048576): 256,
+               ("nvfp4", 8, 4096): 32, ("nvfp4", 1, 32768): 256, ("nvfp4", 4, 8192): 64,
+               ("nvfp4", 2, 16384): 128, ("nvfp4", 16, 4096): 32, ("nvfp4", 32, 1024): 8}
+    for (fmt, batch, ctx), want in fastest.items():
+        p = _p(batch=batch, max_kv_len=ctx, pool_tokens=batch * ctx, page_size=64)
+        code = qk.MLAQ_NVFP4 if fmt == "nvfp4" else qk.MLAQ_FP8_E4M3
+        assert qk.mlaq_decode_num_splits(p, code) == want, (fmt, batch, ctx)
+
+
 def test_split_token_cap():
     """No split covers more than MLAQ_MAX_SPLIT_TOKENS tokens: forced counts below
     ceil(max_kv_len / cap) are rejected before any launch, and the automatic plan never goes there."""

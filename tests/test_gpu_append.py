@@ -133,14 +133,14 @@ def test_append_nan_row_and_empty_request():
     assert_parity(out, lse, ref_out, ref_lse, requests=[2], tag="append nan")
 
 
-@pytest.mark.parametrize("splits", [0, 1024])
-def test_append_with_the_most_splits(splits):
-    """A fused append at batch 1 and 32K context, where the automatic plan and a forced count both
-    reach MLAQ_MAX_SPLITS (1,024) splits: the merge then reduces 1,025 partial slots per request,
-    the new token's being the last."""
+@pytest.mark.parametrize("ctx, splits", [(262144, 0), (32768, 1024)])
+def test_append_with_the_most_splits(ctx, splits):
+    """A fused append at batch 1 where the split count reaches MLAQ_MAX_SPLITS (1,024): by the
+    automatic plan at 256K context, forced at 32K. The merge then reduces 1,025 partial slots per
+    request, the new token's being the last."""
     qk = _qk()
-    lens = [32768]
+    lens = [ctx]
     c, src, ref_d, ref_s, rows = _case(lens, 64, seed=47, src_fmt="bf16")
-    p = qk.decode_params(1, 16, 64, 32768, c.nv_data.shape[0], c.w.sm_scale, splits)
+    p = qk.decode_params(1, 16, 64, ctx, c.nv_data.shape[0], c.w.sm_scale, splits)
     assert qk.mlaq_decode_num_splits(p, qk.MLAQ_NVFP4) == 1024
     _check(lens, 64, seed=47, src_fmt="bf16", splits=(splits,))

@@ -31,10 +31,10 @@ def _same(a, b):
 def test_noalloc_matches_the_workspace_call():
     import quantized_kv_paged_amd as qk
     rng = np.random.default_rng(60)
-    # (lengths, page size, max_kv_len, forced splits): the first case's automatic plan (41 splits x 49
-    # requests) outgrows the scratch, so the call runs the largest count that fits (31); then a
-    # multi-split case at the automatic plan, a forced count, and a one-split case
-    cases = [(list(rng.integers(0, 1500, 49)), 64, 32768, 0), ([3000, 1500, 0, 700], 64, 3000, 0),
+    # (lengths, page size, max_kv_len, forced splits): the first case's automatic plan (15 splits x 129
+    # requests, 63.7 MB of partials) outgrows the scratch, so the call runs the largest count that
+    # fits (11); then a multi-split case at the automatic plan, a forced count, and a one-split case
+    cases = [(list(rng.integers(0, 1500, 129)), 64, 32768, 0), ([3000, 1500, 0, 700], 64, 3000, 0),
              ([2048, 5], 64, 2048, 7), ([300, 17], 16, 300, 1)]
     for i, (lens, P, mk, splits) in enumerate(cases):
         c = build_case("nvfp4", lens, P, seed=61 + i, outlier_p=0.01)
