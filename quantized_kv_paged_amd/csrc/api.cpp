@@ -240,8 +240,11 @@ mlaq_status extend_layout(const mlaq_extend_params* p, ExtendLayout& L) {
   L.indptr_off = L.lens_off + align256((size_t)p->num_q * 4);
   L.part_off = L.indptr_off + align256((size_t)(p->num_q + 1) * 4);
   {
-    // KV splits so that the workgroups (one per kXT chunk tokens of a request and 16-head
-    // group, one per CU) cover the CUs at least once; each split takes whole 32-row tiles
+    // KV splits: workgroups (one per kXT chunk tokens of a request and 16-head group, one per CU)
+    // run in rounds of the CUs; each split takes whole 32-row tiles.  The automatic count
+    // minimizes rounds x tiles per split (in tile-times) plus the partials each extra split
+    // writes and the merge reads (measured: about 0.0105 tile-times per query token and 16-head
+    // group and split), so the last round is not left mostly idle
     const int tile = mlaq::extend_attn_tile_rows(), per_group = mlaq::extend_attn_tokens_per_group();
     const int max_tiles = (int)((span + tile - 1) / tile);
     const int64_t groups = (int64_t)p->batch * ((p->max_chunk_len + per_group - 1) / per_group) * (p->num_heads / 16);
@@ -250,8 +253,18 @@ mlaq_status extend_layout(const mlaq_extend_params* p, ExtendLayout& L) {
     if (p->num_splits > 0 && p->num_splits < smin)
       return fail(MLAQ_ERR_SHAPE, "num_splits %d leaves chunks longer than %d rows (%lld rows need at least %d splits)",
                   p->num_splits, MLAQ_MAX_SPLIT_TOKENS, (long long)span, smin);
-    int s_ = p->num_splits > 0 ? p->num_splits
-                               : (int)std::min<int64_t>(MLAQ_MAX_SPLITS, groups > 0 ? (mlaq::kComputeUnits + groups - 1) / groups : 1);
+    int s_ = p->num_splits;
+    if (s_ <= 0) {
+      s_ = smin;
+      double best = std::numeric_limits<double>::infinity();
+      const int smax = std::max(smin, std::min(MLAQ_MAX_SPLITS, std::max(1, max_tiles)));
+      for (int s = smin; s <= smax; ++s) {
+        const double rounds = std::ceil((double)groups * s / mlaq::kComputeUnits);
+        const double per = std::ceil((double)max_tiles / s);
+        const double cost = rounds * per + (s > 1 ? 0.0105 * p->num_q * (p->num_heads / 16) * s : 0.0);
+        if (cost < best - 1e-9) { best = cost; s_ = s; }
+      }
+    }
     s_ = std::max(smin, std::max(1, std::min(s_, std::max(1, max_tiles))));
     L.tiles_per_split = std::max(1, (max_tiles + s_ - 1) / s_);
     L.tsplits = (max_tiles + L.tiles_per_split - 1) / L.tiles_per_split;

@@ -5,12 +5,13 @@
 // token in its own decode workgroup re-reads and re-converts every row once per token; here a
 // workgroup takes kXT consecutive chunk tokens of one request (a wave pair per token: the two
 // halves of the 576 score dims and of the 512 value dims, as in the decode kernel) and walks
-// the rows once for all of them: per tile of 32 rows, the 512 threads load the FP8 rows,
-// convert them to fp16 into an LDS tile shared by the 8 waves (rows loaded two tiles ahead,
-// converted into the next of three LDS buffers one tile ahead), and every wave reads its K
-// operands and its transposed V operands from it.  The score swap's barrier is the only one
-// per tile: with three tile buffers, the buffer a wave fills at the start of tile k was last
-// read in tile k - 2, which every wave finished before the swap barrier of tile k - 1.
+// the rows once for all of them: per tile of 32 rows, the 768 threads load the FP8 rows,
+// convert them to fp16 into an LDS tile shared by the 12 waves (rows loaded two tiles ahead,
+// converted into the other of two LDS buffers one tile ahead), and every wave reads its K
+// operands and its transposed V operands from it.  Twelve waves are three per SIMD (at most
+// 168 registers each); two tile buffers and the score swaps fit 128 KB of LDS.  Each tile has
+// two barriers: the score swap's, after which the tile stored at its start is visible, and
+// one at its end, after which the buffer its PV products read may be refilled.
 // Token i of the request masks rows >= P + i + 1.  A single split writes out and lse;
 // several splits write decode-layout partials for the merge kernel.
 #include "device_common.h"
@@ -18,14 +19,14 @@
 
 namespace mlaq {
 
-constexpr int kXT = 4;                          // chunk tokens per workgroup
+constexpr int kXT = 6;                          // chunk tokens per workgroup
 constexpr int kXWaves = 2 * kXT;
-constexpr int kXThreads = 64 * kXWaves;         // 512
+constexpr int kXThreads = 64 * kXWaves;         // 768
 constexpr int kXRows = 32;                      // rows per tile (two 16-row MFMA blocks)
 constexpr int kXRowB = 1280;                    // LDS bytes per tile row: 576 fp16 dims in 80 chunks
 constexpr int kXTileB = kXRows * kXRowB;        // 40 KB
 constexpr int kXSwapW = 2 * 64 * 16;            // a wave's partial scores (2 KB)
-constexpr int kXSmem = 3 * kXTileB + 2 * kXWaves * kXSwapW;   // 152 KB: one workgroup per CU
+constexpr int kXSmem = 2 * kXTileB + 2 * kXWaves * kXSwapW;   // 128 KB: one workgroup per CU
 constexpr float kXMinusBig = -3.0e38f;
 constexpr float kXSlack = 8.0f;
 static_assert(kXSmem <= 160 * 1024, "LDS");
@@ -69,7 +70,7 @@ __global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArg
 
   const uint8_t* reg = a.ws_rows + (int64_t)b * a.region_rows * kD;
   char* const tiles = smem;
-  float* const sX = reinterpret_cast<float*>(smem + 3 * kXTileB);
+  float* const sX = reinterpret_cast<float*>(smem + 2 * kXTileB);
 
   // tile loader: thread u of 1152 (16-byte groups) takes row u % 32, dims 16(u / 32) .. +15;
   // rows at or past rows_blk read zeros (descriptor limit)
@@ -154,9 +155,9 @@ __global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArg
 #pragma unroll
   for (int nt = 0; nt < 16; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // pipeline: tile k is in LDS buffer k % 3; the rows of tile k + 1 arrived in registers during
-  // tile k - 1 and are converted into buffer (k + 1) % 3 at the start of tile k (its last
-  // readers, in tile k - 2, passed the swap barrier of tile k - 1), and they are visible to
+  // pipeline: tile k is in LDS buffer k % 2; the rows of tile k + 1 arrived in registers during
+  // tile k - 1 and are converted into buffer (k + 1) % 2 at the start of tile k (its last
+  // readers, in tile k - 1, passed the end barrier of tile k - 1), and they are visible to
   // every wave after the swap barrier of tile k; then the rows of tile k + 2 are loaded.  The
   // score swap buffers alternate with the tiles, as in the decode kernel
   if (ntiles > 0) {
@@ -166,12 +167,12 @@ __global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArg
     __syncthreads();
   }
   for (int k = 0; k < ntiles; ++k) {
-    const int tt = tt0 + k, buf = k & 1, tb3 = k % 3;
+    const int tt = tt0 + k, buf = k & 1;
     if (k + 1 < ntiles) {
-      store(tb3 == 2 ? 0 : tb3 + 1);
+      store(buf ^ 1);
       if (k + 2 < ntiles) load(tt + 2);
     }
-    const char* tile = tiles + tb3 * kXTileB;
+    const char* tile = tiles + buf * kXTileB;
     f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int kb = 0; kb < 9; ++kb)
@@ -238,6 +239,7 @@ __global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArg
       const i16x8 v = i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       o[nt] = mfma16x16x32(pop, __builtin_bit_cast(f16x8, v), o[nt]);
     }
+    __syncthreads();   // every wave is done with this tile's buffer
   }
 
   // ---- outputs of this token: O for heads 4g + i, dims 256dh + 16nt + l16; (m, l) for head l16
