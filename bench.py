@@ -533,7 +533,9 @@ def nvfp4_32k_legs(bn, w, ctx):
                                    nvp[l][1], 1.0, d["indptr"].data_ptr(), d["indices"].data_ptr(), epl.data_ptr(),
                                    eslots.data_ptr(), eout.data_ptr(), else_.data_ptr(), ews.data_ptr(), ews.numel(),
                                    strm))
-        t = bn.timed(estep, n, steps=10, warmup=3)
+        # 20 warm-up calls (about 40 ms of MFMA-bound work) bring the clocks to where a sustained
+        # run holds them; 3 left the first timed calls up to 10 % slow
+        t = bn.timed(estep, n, steps=20, warmup=20)
         flops = EB * sum(2 * w.heads * (EP + i + 1) * (576 + 512) for i in range(EC))
         attn_us = t["split_us"] + t["merge_us"]
         res[kind] = {"requests": EB, "prefix_tokens": EP, "chunk_tokens": EC, "call_us": round(t["step_us"], 1),
