@@ -540,6 +540,16 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
     MLAQ_QK_STEP(0) MLAQ_QK_STEP(1) MLAQ_QK_STEP(2) MLAQ_QK_STEP(3) MLAQ_QK_STEP(4)
     MLAQ_QK_STEP(5) MLAQ_QK_STEP(6) MLAQ_QK_STEP(7) MLAQ_QK_STEP(8)
 #undef MLAQ_QK_STEP
+    // issue order of the 18 (k-block, token block) steps: about one step's conversion (10 VALU),
+    // then one product and one value-tile write, so every product overlaps the next step's
+    // conversion (measured: split kernel 1-2 % faster from HBM, 6 % with the KV in L2, than the
+    // compiler's own order)
+#pragma unroll
+    for (int i = 0; i < 9 * kBlocks; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);   // VALU
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);    // LDS write
+    }
     // the raw tile is converted: its registers take the loads of the next tile, which
     // are in flight during this tile's softmax and PV and the next tiles
     // wave priority: the conversion and QK stretch runs at the highest priority, so that
