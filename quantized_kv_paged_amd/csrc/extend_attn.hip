@@ -7,11 +7,10 @@
 // halves of the 576 score dims and of the 512 value dims, as in the decode kernel) and walks
 // the rows once for all of them: per tile of 32 rows, the 768 threads load the FP8 rows,
 // convert them to fp16 into an LDS tile shared by the 12 waves (rows loaded two tiles ahead,
-// converted into the other of two LDS buffers one tile ahead), and every wave reads its K
+// converted into the next of three LDS buffers one tile ahead), and every wave reads its K
 // operands and its transposed V operands from it.  Twelve waves are three per SIMD (at most
-// 168 registers each); two tile buffers and the score swaps fit 128 KB of LDS.  Each tile has
-// two barriers: the score swap's, after which the tile stored at its start is visible, and
-// one at its end, after which the buffer its PV products read may be refilled.
+// 168 registers each); three tile buffers and two sets of score swaps fill 156 KB of LDS, so
+// that one barrier per tile (the score swap's) orders everything: see the loop.
 // Token i of the request masks rows >= P + i + 1.  A single split writes out and lse;
 // several splits write decode-layout partials for the merge kernel.
 #include "device_common.h"
@@ -23,20 +22,34 @@ constexpr int kXT = 6;                          // chunk tokens per workgroup
 constexpr int kXWaves = 2 * kXT;
 constexpr int kXThreads = 64 * kXWaves;         // 768
 constexpr int kXRows = 32;                      // rows per tile (two 16-row MFMA blocks)
-constexpr int kXRowB = 1280;                    // LDS bytes per tile row: 576 fp16 dims in 80 chunks
-constexpr int kXTileB = kXRows * kXRowB;        // 40 KB
+constexpr int kXRowB = 1152;                    // LDS bytes per tile row: 576 fp16 dims in 72 chunks
+constexpr int kXTileB = kXRows * kXRowB;        // 36 KB
+constexpr int kXBufs = 3;                       // tile buffers
 constexpr int kXSwapW = 2 * 64 * 16;            // a wave's partial scores (2 KB)
-constexpr int kXSmem = 2 * kXTileB + 2 * kXWaves * kXSwapW;   // 128 KB: one workgroup per CU
+constexpr int kXSmem = kXBufs * kXTileB + 2 * kXWaves * kXSwapW;   // 156 KB: one workgroup per CU
 constexpr float kXMinusBig = -3.0e38f;
 constexpr float kXSlack = 8.0f;
 static_assert(kXSmem <= 160 * 1024, "LDS");
 
-// Tile row r, 16-byte chunk c (dims 8c .. 8c+7) lives at chunk (c & ~15) | ((c & 15) ^ s(r)),
-// s(r) = x ^ 2x (mod 16), x = r mod 16: rows start on 256-byte boundaries (1280 = 5 * 256), so
-// the K-operand reads (16 rows x 4 chunks per instruction), the transposed V reads and the
-// row-major tile writes below each spread over all 64 banks (checked by enumeration).
-__device__ __forceinline__ int xswz(int r) { const int x = r & 15; return (x ^ (x << 1)) & 15; }
-__device__ __forceinline__ int xoff(int r, int c) { return r * kXRowB + 16 * ((c & ~15) | ((c & 15) ^ xswz(r))); }
+// Tile row r, 16-byte chunk c (dims 8c .. 8c+7) lives at chunk (c & ~15) | ((c & 15) ^ s(r))
+// for c < 64 and at 64 + ((c & 7) ^ (s(r) & 7)) for the rope chunks, in unpadded 1152-byte
+// rows (odd rows start half-way through the 64 banks).  As its bank-conflict counters show, the
+// LDS serves a 16-byte read or write in groups of 16 lanes (lanes 8i .. 8i+7 with 8i+32 ..
+// 8i+39) and the 8-byte transposed read in groups of 32 lanes; here those groups touch 8
+// consecutive rows at chunks c and c ^ 4 (K operands), c and c ^ 2 (tile writes), c and c ^ 1
+// (V operands).  s(r) for r = 0 .. 7 is
+// 0, 11, 9, 14, 12, 2, 5, 7: with the odd rows' half-way start these are the eight 4-bit values
+// of even weight, of which no two differ in exactly one bit, so every such group spreads over
+// all 64 banks (checked by enumeration; the low 3 bits do the same for the rope chunks).
+__device__ __forceinline__ int xswz(int r) { return (int)((0x752ce9b0u >> (4 * (r & 7))) & 15u); }
+// A value the compiler treats as new in every tile: the per-lane operand addresses derived from
+// it are formed where they are used instead of being held in registers across the tile loop,
+// which leaves the registers for reading V operands ahead of their products.
+__device__ __forceinline__ int opaque(int x) { asm volatile("" : "+v"(x)); return x; }
+__device__ __forceinline__ int xoff(int r, int c) {
+  const int s = xswz(r);
+  return r * kXRowB + 16 * (c < 64 ? ((c & ~15) | ((c & 15) ^ s)) : (64 + ((c & 7) ^ (s & 7))));
+}
 
 __global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kXSmem];
@@ -70,7 +83,7 @@ __global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArg
 
   const uint8_t* reg = a.ws_rows + (int64_t)b * a.region_rows * kD;
   char* const tiles = smem;
-  float* const sX = reinterpret_cast<float*>(smem + 2 * kXTileB);
+  float* const sX = reinterpret_cast<float*>(smem + kXBufs * kXTileB);
 
   // tile loader: thread u of 1152 (16-byte groups) takes row u % 32, dims 16(u / 32) .. +15;
   // rows at or past rows_blk read zeros (descriptor limit)
@@ -141,13 +154,13 @@ __global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArg
     }
   }
 
-  // lane bases: K operand of k-block kb, block tb = qb ^ 16(8((kb >> 1) & 1) + (kb & 1)) +
-  // 256(kb >> 2) + 16 kXRowB tb (kb < 8), qb8 for the rope k-block; V operand of dims
-  // 256dh + 16nt + 4q of rows 16tb + 4g + i = (vrb ^ 32(nt & 7)) + 256(nt >> 3) + 16 kXRowB tb
-  const int qb = l16 * kXRowB + 16 * ((2 * grp) ^ xswz(l16)) + 512 * dh;
-  const int qb8 = l16 * kXRowB + 1024 + 16 * ((4 * dh + grp) ^ xswz(l16));
+  // lane bases: K operand of k-block kb, block tb = qrow + 256(kb >> 2) + (qx ^ 16(8((kb >> 1)
+  // & 1) + (kb & 1))) + 16 kXRowB tb (kb < 8), qb8 for the rope k-block; V operand of dims
+  // 256dh + 16nt + 4q of rows 16tb + 4g + i = vrow_b + 256(nt >> 3) + (vx ^ 32(nt & 7)) + 16 kXRowB tb
+  const int qrow = l16 * kXRowB + 512 * dh, qx = 16 * ((2 * grp) ^ xswz(l16));
+  const int qb8 = l16 * kXRowB + 1024 + 16 * ((4 * dh + grp) ^ (xswz(l16) & 7));
   const int q4 = l16 & 3, vrow = 4 * grp + (l16 >> 2);
-  const int vrb = vrow * kXRowB + 16 * ((q4 >> 1) ^ xswz(vrow)) + 8 * (q4 & 1) + 512 * dh;
+  const int vrow_b = vrow * kXRowB + 8 * (q4 & 1) + 512 * dh, vx = 16 * ((q4 >> 1) ^ xswz(vrow));
 
   // m for head l16; l_run the sum of the lane's own probabilities of head l16
   float m_run = kXMinusBig, l_run = 0.0f;
@@ -155,30 +168,34 @@ __global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArg
 #pragma unroll
   for (int nt = 0; nt < 16; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // pipeline: tile k is in LDS buffer k % 2; the rows of tile k + 1 arrived in registers during
-  // tile k - 1 and are converted into buffer (k + 1) % 2 at the start of tile k (its last
-  // readers, in tile k - 1, passed the end barrier of tile k - 1), and they are visible to
-  // every wave after the swap barrier of tile k; then the rows of tile k + 2 are loaded.  The
-  // score swap buffers alternate with the tiles, as in the decode kernel
+  // pipeline, one barrier per tile (the score swap's): tile k is in LDS buffer k % 3; the rows
+  // of tile k + 1 arrived in registers during tile k - 1 and are converted into buffer
+  // (k + 1) % 3 at the start of tile k (its last readers, the products of tile k - 2, ran before
+  // the swap barrier of tile k - 1, which every wave has passed), and they are visible to every
+  // wave after the swap barrier of tile k; then the rows of tile k + 2 are loaded.  The score
+  // swaps alternate between two buffers: swap buffer k % 2 is written again in tile k + 2, after
+  // the swap barrier of tile k + 1, which its readers in tile k reach only after reading it
   if (ntiles > 0) {
     load(tt0);
     store(0);
     if (ntiles > 1) load(tt0 + 1);
     __syncthreads();
   }
+  int buf = 0;
   for (int k = 0; k < ntiles; ++k) {
-    const int tt = tt0 + k, buf = k & 1;
+    const int tt = tt0 + k, nbuf = buf == kXBufs - 1 ? 0 : buf + 1;
     if (k + 1 < ntiles) {
-      store(buf ^ 1);
+      store(nbuf);
       if (k + 2 < ntiles) load(tt + 2);
     }
     const char* tile = tiles + buf * kXTileB;
+    const int qxk = opaque(qx), qb8k = opaque(qb8);
     f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int kb = 0; kb < 9; ++kb)
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
-        const int off = kb < 8 ? ((qb ^ (16 * (8 * ((kb >> 1) & 1) + (kb & 1)))) + 256 * (kb >> 2)) : qb8;
+        const int off = kb < 8 ? qrow + 256 * (kb >> 2) + (qxk ^ (16 * (8 * ((kb >> 1) & 1) + (kb & 1)))) : qb8k;
         const f16x8 kop = *reinterpret_cast<const f16x8*>(tile + off + 16 * kXRowB * tb);
         sacc[tb] = mfma16x16x32(kop, qop[kb], sacc[tb]);
       }
@@ -186,13 +203,18 @@ __global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArg
     f32x4 sp[2];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
-      sp[tb] = sacc[tb] * score_scale;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (32 * tt + 16 * tb + 4 * grp + j >= vis) sp[tb][j] = -INFINITY;
+      for (int j = 0; j < 4; ++j) sp[tb][j] = sacc[tb][j] * score_scale;
     }
-    float* const xw = sX + (buf * kXWaves + w) * (kXSwapW / 4);
-    const float* const xp = sX + (buf * kXWaves + (w ^ 1)) * (kXSwapW / 4);
+    if (32 * tt + kXRows > P + i0 + 1) {           // uniform: the tile holds a row some token does not see
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (32 * tt + 16 * tb + 4 * grp + j >= vis) sp[tb][j] = -INFINITY;
+    }
+    float* const xw = sX + ((k & 1) * kXWaves + w) * (kXSwapW / 4);
+    const float* const xp = sX + ((k & 1) * kXWaves + (w ^ 1)) * (kXSwapW / 4);
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) *reinterpret_cast<f32x4*>(xw + 256 * tb + 4 * lane) = sp[tb];
     __syncthreads();
@@ -232,14 +254,24 @@ __global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArg
     for (int j = 0; j < 8; j += 2)                 // the rounded probabilities the products use
       rsum = __builtin_amdgcn_fdot2(f16x2{pop[j], pop[j + 1]}, f16x2{(_Float16)1.0f, (_Float16)1.0f}, rsum, false);
     l_run += rsum;   // the lane's own rows; lane groups are added after the last tile
+    const int vxk = opaque(vx);
+    i16x8 vop[16];
 #pragma unroll
     for (int nt = 0; nt < 16; ++nt) {
-      const char* pv = tile + ((vrb ^ (32 * (nt & 7))) + 256 * (nt >> 3));
+      const char* pv = tile + vrow_b + 256 * (nt >> 3) + (vxk ^ (32 * (nt & 7)));
       const i16x4 lo = lds_read_tr16(pv), hi = lds_read_tr16(pv + 16 * kXRowB);
-      const i16x8 v = i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      o[nt] = mfma16x16x32(pop, __builtin_bit_cast(f16x8, v), o[nt]);
+      vop[nt] = i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
-    __syncthreads();   // every wave is done with this tile's buffer
+#pragma unroll
+    for (int nt = 0; nt < 16; ++nt) o[nt] = mfma16x16x32(pop, __builtin_bit_cast(f16x8, vop[nt]), o[nt]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);    // V operands read three products ahead
+#pragma unroll
+    for (int i = 0; i < 13; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+    buf = nbuf;
   }
 
   // ---- outputs of this token: O for heads 4g + i, dims 256dh + 16nt + l16; (m, l) for head l16
