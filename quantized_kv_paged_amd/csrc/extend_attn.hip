@@ -3,14 +3,16 @@
 // Extend (NVFP4 article on aitop.news, implementation item 2) attends every chunk token of a
 // request over the same workspace rows (prefix, then the chunk), causally.  Attending each
 // token in its own decode workgroup re-reads and re-converts every row once per token; here a
-// workgroup takes kXT consecutive chunk tokens of one request (a wave pair per token: the two
-// halves of the 576 score dims and of the 512 value dims, as in the decode kernel) and walks
-// the rows once for all of them: per tile of 32 rows, the 768 threads load the FP8 rows,
-// convert them to fp16 into an LDS tile shared by the 12 waves (rows loaded two tiles ahead,
-// converted into the next of three LDS buffers one tile ahead), and every wave reads its K
-// operands and its transposed V operands from it.  Twelve waves are three per SIMD (at most
-// 168 registers each); three tile buffers and two sets of score swaps fill 156 KB of LDS, so
-// that one barrier per tile (the score swap's) orders everything: see the loop.
+// workgroup of 8 waves takes 8 consecutive chunk tokens of one request, one wave per token over
+// all 576 score dims and all 512 value dims (no partial scores to exchange), and walks the rows
+// once for all of them: per tile of 32 rows the 512 threads load the FP8 rows (two tiles
+// ahead) and convert them to fp16 into the next of two LDS tile buffers one tile ahead; every
+// wave reads its K operands and its transposed V operands from the current one.  A wave holds
+// its token's 16 x 512 fp32 accumulator (128 registers) and the query's dims 256 .. 575 (40);
+// dims 0 .. 255 stay in LDS, read with the K operands, so that the V operands of the PV
+// products can be read four products ahead within two waves per SIMD (256 registers).  One
+// barrier per tile, at its end: the buffer the next tile's rows go to was last read before it,
+// and the rows stored at the tile's start are visible after it.
 // Token i of the request masks rows >= P + i + 1.  A single split writes out and lse;
 // several splits write decode-layout partials for the merge kernel.
 #include "device_common.h"
@@ -18,15 +20,16 @@
 
 namespace mlaq {
 
-constexpr int kXT = 6;                          // chunk tokens per workgroup
-constexpr int kXWaves = 2 * kXT;
-constexpr int kXThreads = 64 * kXWaves;         // 768
+constexpr int kXT = 8;                          // chunk tokens per workgroup, one wave each
+constexpr int kXWaves = kXT;
+constexpr int kXThreads = 64 * kXWaves;         // 512
 constexpr int kXRows = 32;                      // rows per tile (two 16-row MFMA blocks)
 constexpr int kXRowB = 1152;                    // LDS bytes per tile row: 576 fp16 dims in 72 chunks
 constexpr int kXTileB = kXRows * kXRowB;        // 36 KB
-constexpr int kXBufs = 3;                       // tile buffers
-constexpr int kXSwapW = 2 * 64 * 16;            // a wave's partial scores (2 KB)
-constexpr int kXSmem = kXBufs * kXTileB + 2 * kXWaves * kXSwapW;   // 156 KB: one workgroup per CU
+constexpr int kXBufs = 2;                       // tile buffers
+constexpr int kXQL = 8;                         // query k-blocks (32 dims each) kept in LDS
+constexpr int kXQW = 16 * 64 * kXQL;            // a wave's LDS query bytes (16 heads x 256 dims fp16)
+constexpr int kXSmem = kXBufs * kXTileB + kXWaves * kXQW;   // 136 KB: one workgroup per CU
 constexpr float kXMinusBig = -3.0e38f;
 constexpr float kXSlack = 8.0f;
 static_assert(kXSmem <= 160 * 1024, "LDS");
@@ -36,20 +39,25 @@ static_assert(kXSmem <= 160 * 1024, "LDS");
 // rows (odd rows start half-way through the 64 banks).  As its bank-conflict counters show, the
 // LDS serves a 16-byte read or write in groups of 16 lanes (lanes 8i .. 8i+7 with 8i+32 ..
 // 8i+39) and the 8-byte transposed read in groups of 32 lanes; here those groups touch 8
-// consecutive rows at chunks c and c ^ 4 (K operands), c and c ^ 2 (tile writes), c and c ^ 1
-// (V operands).  s(r) for r = 0 .. 7 is
-// 0, 11, 9, 14, 12, 2, 5, 7: with the odd rows' half-way start these are the eight 4-bit values
-// of even weight, of which no two differ in exactly one bit, so every such group spreads over
-// all 64 banks (checked by enumeration; the low 3 bits do the same for the rope chunks).
+// consecutive rows at chunks c and c ^ 2 (K operands and tile writes) or c and c ^ 1 (V
+// operands).  s(r) for r = 0 .. 7 is 0, 11, 9, 14, 12, 2, 5, 7: with the odd rows' half-way
+// start these are the eight 4-bit values of even weight, of which no two differ in exactly one
+// bit, so every such group spreads over all 64 banks (checked by enumeration; the low 3 bits do
+// the same for the rope chunks).
 __device__ __forceinline__ int xswz(int r) { return (int)((0x752ce9b0u >> (4 * (r & 7))) & 15u); }
-// A value the compiler treats as new in every tile: the per-lane operand addresses derived from
-// it are formed where they are used instead of being held in registers across the tile loop,
-// which leaves the registers for reading V operands ahead of their products.
-__device__ __forceinline__ int opaque(int x) { asm volatile("" : "+v"(x)); return x; }
 __device__ __forceinline__ int xoff(int r, int c) {
   const int s = xswz(r);
   return r * kXRowB + 16 * (c < 64 ? ((c & ~15) | ((c & 15) ^ s)) : (64 + ((c & 7) ^ (s & 7))));
 }
+// A wave's LDS query: head h's row of 512 bytes, chunk c (dims 8c .. 8c+7) at (c & ~15) |
+// ((c & 15) ^ f(h)), f(h) for h = 0 .. 7 = 0, 1, 4, 5, 8, 9, 12, 13: a read group takes heads h0 ..
+// h0+7 at chunks c and c ^ 2, and no two values of f differ by 2 in that bit, so it spreads over
+// all banks (checked by enumeration).
+__device__ __forceinline__ int qswz(int h) { return (int)((0xdc985410u >> (4 * (h & 7))) & 15u); }
+// A value the compiler treats as new in every tile: the per-lane operand addresses derived from
+// it are formed where they are used instead of being held in registers across the tile loop,
+// which leaves the registers for reading V operands ahead of their products.
+__device__ __forceinline__ int opaque(int x) { asm volatile("" : "+v"(x)); return x; }
 
 __global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kXSmem];
@@ -61,7 +69,6 @@ __global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArg
   const int H = a.num_heads, HG = H >> 4;        // 16-head groups, each its own workgroups
   const int split = blockIdx.z / HG, hg = blockIdx.z - split * HG;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, grp = lane >> 4;
-  const int pi = w >> 1, dh = w & 1;             // token of the pair, dim half
 
   // ---- request bounds (the checks of the view builder; invalid requests were given NaN there)
   const int P = a.prefix_lens[b], q0 = a.qo_indptr[b], C = a.qo_indptr[b + 1] - q0;
@@ -71,9 +78,9 @@ __global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArg
                   (int64_t)(p1 - p0) * a.page_size >= (int64_t)P;
   const int i0 = blk * kXT;
   if (!ok || i0 >= C) return;                    // uniform
-  const int ci = i0 + pi;                        // this pair's chunk token
+  const int ci = i0 + w;                         // this wave's chunk token
   const bool tok = ci < C;                       // wave-uniform
-  const int t = q0 + (tok ? ci : C - 1);         // its query row (a valid one for idle pairs)
+  const int t = q0 + (tok ? ci : C - 1);         // its query row (a valid one for idle waves)
   const int vis = tok ? P + ci + 1 : 0;          // rows it sees
   const int rows_blk = P + min(C, i0 + kXT);     // rows any token of the block sees
   const int tiles_all = (rows_blk + kXRows - 1) / kXRows;
@@ -83,10 +90,10 @@ __global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArg
 
   const uint8_t* reg = a.ws_rows + (int64_t)b * a.region_rows * kD;
   char* const tiles = smem;
-  float* const sX = reinterpret_cast<float*>(smem + kXBufs * kXTileB);
+  char* const qlds = smem + kXBufs * kXTileB + w * kXQW;   // this wave's query, k-blocks 0 .. kXQL - 1
 
-  // tile loader: thread u of 1152 (16-byte groups) takes row u % 32, dims 16(u / 32) .. +15;
-  // rows at or past rows_blk read zeros (descriptor limit)
+  // tile loader: thread u of 1152 (16-byte groups; three rounds of 512, the last one partial)
+  // takes row u % 32, dims 16(u / 32) .. +15; rows at or past rows_blk read zeros (descriptor limit)
   u32x4 raw[3];
   auto load = [&](int tt) __attribute__((always_inline)) {
     const int r0 = tt * kXRows;
@@ -122,19 +129,20 @@ __global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArg
     }
   };
 
-  // this token's query half as fp16 (exact after a power-of-two prescale per head and half,
-  // folded into the score scale), k-block kb of lane (g, head l16) = dims xdim(kb) .. +7
-  auto xdim = [&](int kb) { return kb == 8 ? 512 + 32 * dh + 8 * grp : 256 * dh + 64 * (kb >> 1) + 16 * grp + 8 * (kb & 1); };
-  f16x8 qop[9];
+  // this token's query as fp16 (exact after a power-of-two prescale per head, folded into the
+  // score scale), k-block kb of lane (g, head l16) = dims 32kb + 8g .. +7: blocks 0 .. kXQL - 1
+  // go to LDS, the others stay in registers
+  auto xdim = [&](int kb) { return 32 * kb + 8 * grp; };
+  f16x8 qop[18 - kXQL];
   float score_scale;
   {
     const uint16_t* qrow = a.q + ((int64_t)t * H + 16 * hg + l16) * kD;
-    u32x4 qraw[9];
+    u32x4 qraw[18];
 #pragma unroll
-    for (int kb = 0; kb < 9; ++kb) qraw[kb] = *reinterpret_cast<const u32x4*>(qrow + xdim(kb));
+    for (int kb = 0; kb < 18; ++kb) qraw[kb] = *reinterpret_cast<const u32x4*>(qrow + xdim(kb));
     uint32_t mx = 0;
 #pragma unroll
-    for (int kb = 0; kb < 9; ++kb)
+    for (int kb = 0; kb < 18; ++kb)
 #pragma unroll
       for (int e = 0; e < 4; ++e) mx = max(mx, max((qraw[kb][e] & 0x7fffu) << 16, qraw[kb][e] & 0x7fff0000u));
     const float qmax = rows_max(u2f(mx));
@@ -143,38 +151,43 @@ __global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArg
     const float up = u2f((uint32_t)(127 + sh) << 23);
     score_scale = a.score_scale * u2f((uint32_t)(127 - sh) << 23);
 #pragma unroll
-    for (int kb = 0; kb < 9; ++kb) {
+    for (int kb = 0; kb < 18; ++kb) {
       f16x8 qv;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         qv[2 * e] = (_Float16)(u2f(qraw[kb][e] << 16) * up);
         qv[2 * e + 1] = (_Float16)(u2f(qraw[kb][e] & 0xffff0000u) * up);
       }
-      qop[kb] = qv;
+      if (kb < kXQL) {
+        const int c = 4 * kb + grp;
+        *reinterpret_cast<f16x8*>(qlds + l16 * (64 * kXQL) + 16 * ((c & ~15) | ((c & 15) ^ qswz(l16)))) = qv;
+      } else {
+        qop[kb - kXQL] = qv;
+      }
     }
   }
 
-  // lane bases: K operand of k-block kb, block tb = qrow + 256(kb >> 2) + (qx ^ 16(8((kb >> 1)
-  // & 1) + (kb & 1))) + 16 kXRowB tb (kb < 8), qb8 for the rope k-block; V operand of dims
-  // 256dh + 16nt + 4q of rows 16tb + 4g + i = vrow_b + 256(nt >> 3) + (vx ^ 32(nt & 7)) + 16 kXRowB tb
-  const int qrow = l16 * kXRowB + 512 * dh, qx = 16 * ((2 * grp) ^ xswz(l16));
-  const int qb8 = l16 * kXRowB + 1024 + 16 * ((4 * dh + grp) ^ (xswz(l16) & 7));
+  // lane bases: K operand of k-block kb (chunk 4kb + g, or 64 + 4(kb - 16) + g for the rope),
+  // rows block tb = krow + 256(kb >> 2) + (kx ^ 64(kb & 3)) + 16 kXRowB tb (kb < 16), krow + 1024 +
+  // (kx8 ^ 64(kb - 16)) + 16 kXRowB tb (rope); LDS query block kb = 512 l16 + 256(kb >> 2) + (qx ^
+  // 64(kb & 3)); V operand of dims 16nt + 4q of rows 16tb + 4g + i = vrow_b + 256(nt >> 3) + (vx ^
+  // 32(nt & 7)) + 16 kXRowB tb
+  const int krow = l16 * kXRowB, kx = 16 * (grp ^ xswz(l16)), kx8 = 16 * (grp ^ (xswz(l16) & 7));
+  const int qx = 16 * (grp ^ qswz(l16));
   const int q4 = l16 & 3, vrow = 4 * grp + (l16 >> 2);
-  const int vrow_b = vrow * kXRowB + 8 * (q4 & 1) + 512 * dh, vx = 16 * ((q4 >> 1) ^ xswz(vrow));
+  const int vrow_b = vrow * kXRowB + 8 * (q4 & 1), vx = 16 * ((q4 >> 1) ^ xswz(vrow));
 
   // m for head l16; l_run the sum of the lane's own probabilities of head l16
   float m_run = kXMinusBig, l_run = 0.0f;
-  f32x4 o[16];
+  f32x4 o[32];
 #pragma unroll
-  for (int nt = 0; nt < 16; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int nt = 0; nt < 32; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // pipeline, one barrier per tile (the score swap's): tile k is in LDS buffer k % 3; the rows
-  // of tile k + 1 arrived in registers during tile k - 1 and are converted into buffer
-  // (k + 1) % 3 at the start of tile k (its last readers, the products of tile k - 2, ran before
-  // the swap barrier of tile k - 1, which every wave has passed), and they are visible to every
-  // wave after the swap barrier of tile k; then the rows of tile k + 2 are loaded.  The score
-  // swaps alternate between two buffers: swap buffer k % 2 is written again in tile k + 2, after
-  // the swap barrier of tile k + 1, which its readers in tile k reach only after reading it
+  // pipeline, one barrier per tile: tile k is in LDS buffer k % 2; the rows of tile k + 1
+  // arrived in registers during tile k - 1 and are converted into buffer (k + 1) % 2 at the
+  // start of tile k (its last readers, the products of tile k - 1, ran before the barrier that
+  // ended tile k - 1), and they are visible to every wave after the barrier that ends tile k;
+  // then the rows of tile k + 2 are loaded
   if (ntiles > 0) {
     load(tt0);
     store(0);
@@ -183,50 +196,41 @@ __global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArg
   }
   int buf = 0;
   for (int k = 0; k < ntiles; ++k) {
-    const int tt = tt0 + k, nbuf = buf == kXBufs - 1 ? 0 : buf + 1;
+    const int tt = tt0 + k, nbuf = buf ^ 1;
     if (k + 1 < ntiles) {
       store(nbuf);
       if (k + 2 < ntiles) load(tt + 2);
     }
     const char* tile = tiles + buf * kXTileB;
-    const int qxk = opaque(qx), qb8k = opaque(qb8);
+    const int kxk = opaque(kx), kx8k = opaque(kx8), qxk = opaque(qx);
     f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int kb = 0; kb < 9; ++kb)
+    for (int kb = 0; kb < 18; ++kb)
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb) {
-        const int off = kb < 8 ? qrow + 256 * (kb >> 2) + (qxk ^ (16 * (8 * ((kb >> 1) & 1) + (kb & 1)))) : qb8k;
+        // chunk 4kb + g (value dims) or 64 + 4(kb - 16) + g (rope) of row l16 + 16tb
+        const int off = kb < 16 ? krow + 256 * (kb >> 2) + (kxk ^ (64 * (kb & 3))) : krow + 1024 + (kx8k ^ (64 * (kb - 16)));
         const f16x8 kop = *reinterpret_cast<const f16x8*>(tile + off + 16 * kXRowB * tb);
-        sacc[tb] = mfma16x16x32(kop, qop[kb], sacc[tb]);
+        f16x8 qv;
+        if (kb < kXQL) {
+          qv = *reinterpret_cast<const f16x8*>(qlds + l16 * (64 * kXQL) + 256 * (kb >> 2) + (qxk ^ (64 * (kb & 3))));
+        } else {
+          qv = qop[kb - kXQL];
+        }
+        sacc[tb] = mfma16x16x32(kop, qv, sacc[tb]);
       }
-    // scores of this token: lane (g, head l16) holds rows 32tt + 16tb + 4g + j
-    f32x4 sp[2];
+    float sc[8];
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
+    for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sp[tb][j] = sacc[tb][j] * score_scale;
-    }
+      for (int j = 0; j < 4; ++j) sc[4 * tb + j] = sacc[tb][j] * score_scale;
     if (32 * tt + kXRows > P + i0 + 1) {           // uniform: the tile holds a row some token does not see
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          if (32 * tt + 16 * tb + 4 * grp + j >= vis) sp[tb][j] = -INFINITY;
+          if (32 * tt + 16 * tb + 4 * grp + j >= vis) sc[4 * tb + j] = -INFINITY;
     }
-    float* const xw = sX + ((k & 1) * kXWaves + w) * (kXSwapW / 4);
-    const float* const xp = sX + ((k & 1) * kXWaves + (w ^ 1)) * (kXSwapW / 4);
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb) *reinterpret_cast<f32x4*>(xw + 256 * tb + 4 * lane) = sp[tb];
-    __syncthreads();
-    float sc[8];
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
-      const f32x4 sq = *reinterpret_cast<const f32x4*>(xp + 256 * tb + 4 * lane);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sc[4 * tb + j] = sp[tb][j] + sq[j];
-    }
-    // lazy rescale as in the decode kernel: one vote over the lanes' own maxima, the heads'
-    // maxima over their lane groups only when some reference must move
     float lmax = sc[0];
 #pragma unroll
     for (int j = 1; j < 8; ++j) lmax = fmaxf(lmax, sc[j]);
@@ -241,40 +245,40 @@ __global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArg
       for (int i = 0; i < 4; ++i) {
         const float ai = __shfl(alpha, 4 * grp + i);
 #pragma unroll
-        for (int nt = 0; nt < 16; ++nt) o[nt][i] *= ai;
+        for (int nt = 0; nt < 32; ++nt) o[nt][i] *= ai;
       }
     }
     f16x8 pop;
     float rsum = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      pop[j] = (_Float16)fast_exp2(sc[j] - m_run);
-    }
+    for (int j = 0; j < 8; ++j) pop[j] = (_Float16)fast_exp2(sc[j] - m_run);
 #pragma unroll
-    for (int j = 0; j < 8; j += 2)                 // the rounded probabilities the products use
+    for (int j = 0; j < 8; j += 2)
       rsum = __builtin_amdgcn_fdot2(f16x2{pop[j], pop[j + 1]}, f16x2{(_Float16)1.0f, (_Float16)1.0f}, rsum, false);
-    l_run += rsum;   // the lane's own rows; lane groups are added after the last tile
+    l_run += rsum;
+    // PV: the V operands are read four products ahead of their products
     const int vxk = opaque(vx);
-    i16x8 vop[16];
+    i16x8 vop[32];
 #pragma unroll
-    for (int nt = 0; nt < 16; ++nt) {
+    for (int nt = 0; nt < 32; ++nt) {
       const char* pv = tile + vrow_b + 256 * (nt >> 3) + (vxk ^ (32 * (nt & 7)));
       const i16x4 lo = lds_read_tr16(pv), hi = lds_read_tr16(pv + 16 * kXRowB);
       vop[nt] = i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
 #pragma unroll
-    for (int nt = 0; nt < 16; ++nt) o[nt] = mfma16x16x32(pop, __builtin_bit_cast(f16x8, vop[nt]), o[nt]);
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);    // V operands read three products ahead
+    for (int nt = 0; nt < 32; ++nt) o[nt] = mfma16x16x32(pop, __builtin_bit_cast(f16x8, vop[nt]), o[nt]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-    for (int i = 0; i < 13; ++i) {
+    for (int i = 0; i < 28; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __syncthreads();   // every wave is done with this tile's buffer; the next tile is visible
     buf = nbuf;
   }
 
-  // ---- outputs of this token: O for heads 4g + i, dims 256dh + 16nt + l16; (m, l) for head l16
+  // ---- outputs of this token: O for heads 4g + i, dims 16nt + l16; (m, l) for head l16
   l_run = rows_sum(l_run);
   if (!tok) return;
   if (a.num_splits == 1) {
@@ -284,22 +288,22 @@ __global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArg
       const float L = __shfl(l_run, h);
       float f = L > 0.0f ? a.out_scale / L : 0.0f;
       if (L != L) f = L;
-      float* dst = a.out + ((int64_t)t * H + 16 * hg + h) * kDV + 256 * dh + l16;
+      float* dst = a.out + ((int64_t)t * H + 16 * hg + h) * kDV + l16;
 #pragma unroll
-      for (int nt = 0; nt < 16; ++nt) dst[16 * nt] = o[nt][i] * f;
+      for (int nt = 0; nt < 32; ++nt) dst[16 * nt] = o[nt][i] * f;
     }
-    if (a.lse && dh == 0 && grp == 0)
+    if (a.lse && grp == 0)
       a.lse[(int64_t)t * H + 16 * hg + l16] = l_run > 0.0f ? (m_run + __log2f(l_run)) * kLn2
                                                    : (l_run != l_run ? l_run : -INFINITY);
   } else {
     const int64_t slot = ((int64_t)t * a.num_splits + split) * HG + hg;   // the decode partial layout
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float* dst = a.part_o + slot * (16 * kDV) + (4 * grp + i) * kDV + 256 * dh + l16;
+      float* dst = a.part_o + slot * (16 * kDV) + (4 * grp + i) * kDV + l16;
 #pragma unroll
-      for (int nt = 0; nt < 16; ++nt) dst[16 * nt] = o[nt][i];
+      for (int nt = 0; nt < 32; ++nt) dst[16 * nt] = o[nt][i];
     }
-    if (dh == 0 && grp == 0) {
+    if (grp == 0) {
       a.part_ml[slot * 32 + l16] = ntiles > 0 ? m_run : -INFINITY;
       a.part_ml[slot * 32 + 16 + l16] = l_run;
     }

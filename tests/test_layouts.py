@@ -1,9 +1,10 @@
-"""Host checks of the extend attention kernel's LDS tile layout (no GPU): the swizzle table is
-read out of the kernel source, then every (row, 16-byte chunk) slot of the fp16 tile must be
-distinct and inside the tile, and each lane group the LDS serves in one pass (16-byte accesses:
-lanes 8i .. 8i+7 with 8i+32 .. 8i+39; 8-byte transposed reads: 32 consecutive lanes) must touch
-each of the 64 four-byte banks at most once, for the K-operand reads, the transposed V reads
-and the tile writes, with the lane -> (row, chunk) maps the kernel uses."""
+"""Host checks of the extend attention kernel's LDS layouts (no GPU): the swizzle tables are
+read out of the kernel source, then every (row, 16-byte chunk) slot of the fp16 tile and of a
+wave's query area must be distinct and inside its area, and each lane group the LDS serves in
+one pass (16-byte accesses: lanes 8i .. 8i+7 with 8i+32 .. 8i+39; 8-byte transposed reads: 32
+consecutive lanes) must touch each of the 64 four-byte banks at most once, for the K-operand
+reads, the query reads, the transposed V reads and the tile writes, with the lane -> (row,
+chunk) maps the kernel uses."""
 import os
 import re
 
@@ -20,17 +21,20 @@ def _constant(name):
     return int(m.group(1))
 
 
-def _swizzle_table():
-    m = re.search(r"int xswz\(int r\) \{ return \(int\)\(\((0x[0-9a-f]+)u >> \(4 \* \(r & 7\)\)\) & 15u\); \}", open(SRC).read())
-    assert m, "swizzle table not found in the kernel source"
+def _swizzle_table(fn, var):
+    m = re.search(r"int %s\(int %s\) \{ return \(int\)\(\((0x[0-9a-f]+)u >> \(4 \* \(%s & 7\)\)\) & 15u\); \}" % (fn, var, var),
+                  open(SRC).read())
+    assert m, fn + " table not found in the kernel source"
     word = int(m.group(1), 16)
     return [(word >> (4 * r)) & 15 for r in range(8)]
 
 
 ROW_B = _constant("kXRowB")
 ROWS = _constant("kXRows")
-THREADS = 64 * 2 * _constant("kXT")
-S = _swizzle_table()
+QL = _constant("kXQL")
+THREADS = 64 * _constant("kXT")
+S = _swizzle_table("xswz", "r")
+F = _swizzle_table("qswz", "h")
 
 
 def xoff(r, c):
@@ -56,30 +60,37 @@ def _max_bank_load(addrs, nbytes, groups):
     return worst
 
 
-def test_tile_slots_distinct_and_inside():
-    assert ROW_B == 1152 and ROWS == 32
+def qoff(h, c):
+    return h * 64 * QL + 16 * ((c & ~15) | ((c & 15) ^ F[h & 7]))
+
+
+def test_tile_and_query_slots_distinct_and_inside():
+    assert ROW_B == 1152 and ROWS == 32 and QL % 4 == 0
     slots = {xoff(r, c) for r in range(ROWS) for c in range(72)}
     assert len(slots) == ROWS * 72
     assert min(slots) >= 0 and max(slots) + 16 <= ROWS * ROW_B
+    q = {qoff(h, c) for h in range(16) for c in range(4 * QL)}
+    assert len(q) == 16 * 4 * QL and min(q) >= 0 and max(q) + 16 <= 16 * 64 * QL
 
 
-@pytest.mark.parametrize("dh", [0, 1])
-def test_operand_reads_conflict_free(dh):
+def test_operand_reads_conflict_free():
     for tb in range(2):
-        for kb in range(9):   # K operands: lane (g, l16) reads row l16 + 16 tb at one chunk
+        for kb in range(18):  # K operands: lane (g, l16) reads row l16 + 16 tb at one chunk
             a = []
             for lane in range(64):
                 g, l16 = lane >> 4, lane & 15
-                c = 32 * dh + 8 * (kb >> 1) + 2 * g + (kb & 1) if kb < 8 else 64 + 4 * dh + g
-                a.append(xoff(l16 + 16 * tb, c))
+                a.append(xoff(l16 + 16 * tb, 4 * kb + g if kb < 16 else 64 + 4 * (kb - 16) + g))
             assert _max_bank_load(a, 16, G16) == 1, (tb, kb)
+    for kb in range(QL):      # query operands from LDS: lane (g, head l16), chunk 4kb + g
+        a = [qoff(lane & 15, 4 * kb + (lane >> 4)) for lane in range(64)]
+        assert _max_bank_load(a, 16, G16) == 1, kb
     for hi in range(2):
-        for nt in range(16):  # transposed V operands: 8 bytes of row 4g + l16 / 4 (+16)
+        for nt in range(32):  # transposed V operands: 8 bytes of row 4g + l16 / 4 (+16)
             a = []
             for lane in range(64):
                 g, l16 = lane >> 4, lane & 15
                 q4, vrow = l16 & 3, 4 * g + (l16 >> 2)
-                byte = 2 * (256 * dh + 16 * nt + 4 * q4)
+                byte = 2 * (16 * nt + 4 * q4)
                 a.append(xoff(vrow + 16 * hi, byte // 16) + byte % 16)
             assert _max_bank_load(a, 8, G8) == 1, (hi, nt)
 
