@@ -219,6 +219,7 @@ __global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArg
         }
         sacc[tb] = mfma16x16x32(kop, qv, sacc[tb]);
       }
+    // scores of this token: lane (g, head l16) holds rows 32tt + 16tb + 4g + j
     float sc[8];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb)
@@ -231,6 +232,8 @@ __global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArg
         for (int j = 0; j < 4; ++j)
           if (32 * tt + 16 * tb + 4 * grp + j >= vis) sc[4 * tb + j] = -INFINITY;
     }
+    // lazy rescale as in the decode kernel: one vote over the lanes' own maxima, the heads'
+    // maxima over their lane groups only when some reference must move
     float lmax = sc[0];
 #pragma unroll
     for (int j = 1; j < 8; ++j) lmax = fmaxf(lmax, sc[j]);
@@ -253,9 +256,9 @@ __global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArg
 #pragma unroll
     for (int j = 0; j < 8; ++j) pop[j] = (_Float16)fast_exp2(sc[j] - m_run);
 #pragma unroll
-    for (int j = 0; j < 8; j += 2)
+    for (int j = 0; j < 8; j += 2)                 // the rounded probabilities the products use
       rsum = __builtin_amdgcn_fdot2(f16x2{pop[j], pop[j + 1]}, f16x2{(_Float16)1.0f, (_Float16)1.0f}, rsum, false);
-    l_run += rsum;
+    l_run += rsum;   // the lane's own rows; lane groups are added after the last tile
     // PV: the V operands are read four products ahead of their products
     const int vxk = opaque(vx);
     i16x8 vop[32];
