@@ -204,21 +204,28 @@ __global__ __launch_bounds__(kXThreads, 1) void extend_attn_kernel(ExtendAttnArg
     const char* tile = tiles + buf * kXTileB;
     const int kxk = opaque(kx), kx8k = opaque(kx8), qxk = opaque(qx);
     f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    // QK: the K operands (chunk 4kb + g of the value dims, or 64 + 4(kb - 16) + g of the rope, of
+    // row l16 + 16tb) and the LDS query blocks are read five reads ahead of their products
+    f16x8 kops[36], qvs[kXQL];
+#pragma unroll
+    for (int kb = 0; kb < 18; ++kb) {
+      if (kb < kXQL) qvs[kb] = *reinterpret_cast<const f16x8*>(qlds + l16 * (64 * kXQL) + 256 * (kb >> 2) + (qxk ^ (64 * (kb & 3))));
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb) {
+        const int off = kb < 16 ? krow + 256 * (kb >> 2) + (kxk ^ (64 * (kb & 3))) : krow + 1024 + (kx8k ^ (64 * (kb - 16)));
+        kops[2 * kb + tb] = *reinterpret_cast<const f16x8*>(tile + off + 16 * kXRowB * tb);
+      }
+    }
 #pragma unroll
     for (int kb = 0; kb < 18; ++kb)
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        // chunk 4kb + g (value dims) or 64 + 4(kb - 16) + g (rope) of row l16 + 16tb
-        const int off = kb < 16 ? krow + 256 * (kb >> 2) + (kxk ^ (64 * (kb & 3))) : krow + 1024 + (kx8k ^ (64 * (kb - 16)));
-        const f16x8 kop = *reinterpret_cast<const f16x8*>(tile + off + 16 * kXRowB * tb);
-        f16x8 qv;
-        if (kb < kXQL) {
-          qv = *reinterpret_cast<const f16x8*>(qlds + l16 * (64 * kXQL) + 256 * (kb >> 2) + (qxk ^ (64 * (kb & 3))));
-        } else {
-          qv = qop[kb - kXQL];
-        }
-        sacc[tb] = mfma16x16x32(kop, qv, sacc[tb]);
-      }
+      for (int tb = 0; tb < 2; ++tb) sacc[tb] = mfma16x16x32(kops[2 * kb + tb], kb < kXQL ? qvs[kb] : qop[kb - kXQL], sacc[tb]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
+#pragma unroll
+    for (int i = 0; i < 36; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < 36 + kXQL - 5) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
     // scores of this token: lane (g, head l16) holds rows 32tt + 16tb + 4g + j
     float sc[8];
 #pragma unroll
