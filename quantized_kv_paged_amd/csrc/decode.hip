@@ -852,6 +852,73 @@ __global__ __launch_bounds__(kMergeThreads) void mla_merge_kernel(DecodeArgs a) 
     a.lse[(int64_t)b * H + h] = tot > 0.0f ? (M + __log2f(tot)) * kLn2 : (tot != tot ? tot : -INFINITY);
 }
 
+// The same merge for a few splits (at most kRowMergeMax partial slots): one wave per (request,
+// head) row and 8 value dims per lane.  Every lane loads all of the row's (m, l) pairs and its
+// dims of every partial at once, so the row costs one memory latency and no cross-lane step or
+// barrier; the extend call's partials (one row per chunk token and head, two or three splits)
+// take this path, where the chunked kernel above would run tens of thousands of workgroups with
+// most of their lane groups idle.  The sums run over the splits as a pairwise tree.
+constexpr int kRowMergeMax = 8;
+constexpr int kRowMergeRows = 4;   // rows (waves) per workgroup
+
+template <int LO, int N, typename T, int A>
+__device__ __forceinline__ T tree_sum(const T (&x)[A]) {
+  if constexpr (N == 1) return x[LO];
+  else return tree_sum<LO, N / 2>(x) + tree_sum<LO + N / 2, N - N / 2>(x);
+}
+
+__global__ __launch_bounds__(64 * kRowMergeRows) void mla_merge_rows_kernel(DecodeArgs a) {
+  const int H = a.num_heads, HG = H / 16, S = a.part_splits;
+  const int row = blockIdx.x * kRowMergeRows + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= a.batch * H) return;                // wave-uniform
+  const int b = row / H, h = row - b * H, hg = h >> 4, hh = h & 15;
+  const int64_t slot0 = (int64_t)b * S * HG + hg;
+  const int64_t sstride = (int64_t)HG * 16 * kDV;
+  const float* po = a.part_o + slot0 * (16 * kDV) + hh * kDV + 8 * lane;
+  f32x4 v[kRowMergeMax][2];
+  float mv[kRowMergeMax], lv[kRowMergeMax];
+#pragma unroll
+  for (int s = 0; s < kRowMergeMax; ++s) {
+    const float* ml = a.part_ml + (slot0 + (int64_t)s * HG) * 32;
+    v[s][0] = s < S ? *reinterpret_cast<const f32x4*>(po + s * sstride) : f32x4{0.f, 0.f, 0.f, 0.f};
+    v[s][1] = s < S ? *reinterpret_cast<const f32x4*>(po + s * sstride + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    mv[s] = s < S ? ml[hh] : -INFINITY;
+    lv[s] = s < S ? ml[16 + hh] : 0.0f;
+  }
+  const int L = a.kv_lens[b];
+  const int p0 = a.kv_indptr[b], p1 = a.kv_indptr[b + 1];
+  const bool bad = L < (a.app_src ? 1 : 0) || L > a.max_kv_len || p0 < 0 || p1 < p0 ||
+                   p1 > a.kv_indptr[a.batch] || (int64_t)(p1 - p0) * a.page_size < (int64_t)L;
+  float* outp = a.out + ((int64_t)b * H + h) * kDV + 8 * lane;
+  if (bad) {
+    *reinterpret_cast<f32x4*>(outp) = f32x4{NAN, NAN, NAN, NAN};
+    *reinterpret_cast<f32x4*>(outp + 4) = f32x4{NAN, NAN, NAN, NAN};
+    if (a.lse && lane == 0) a.lse[(int64_t)b * H + h] = NAN;
+    return;
+  }
+  float M = mv[0];
+#pragma unroll
+  for (int s = 1; s < kRowMergeMax; ++s) M = fmaxf(M, mv[s]);
+#pragma unroll
+  for (int s = 0; s < kRowMergeMax; ++s) {
+    // a split whose weight is 0 (no rows, or an unused slot) may hold stale data: selected away
+    const float ws = mv[s] == -INFINITY ? 0.0f : exp2f(mv[s] - M);
+    lv[s] *= ws;
+    v[s][0] = ws != 0.0f ? ws * v[s][0] : f32x4{0.f, 0.f, 0.f, 0.f};
+    v[s][1] = ws != 0.0f ? ws * v[s][1] : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  f32x4 v0[kRowMergeMax], v1[kRowMergeMax];
+#pragma unroll
+  for (int s = 0; s < kRowMergeMax; ++s) v0[s] = v[s][0], v1[s] = v[s][1];
+  const float tot = tree_sum<0, kRowMergeMax>(lv);
+  const f32x4 o0 = tree_sum<0, kRowMergeMax>(v0), o1 = tree_sum<0, kRowMergeMax>(v1);
+  const float f = tot > 0.0f ? a.out_scale / tot : (tot != tot ? tot : 0.0f);
+  *reinterpret_cast<f32x4*>(outp) = o0 * f;
+  *reinterpret_cast<f32x4*>(outp + 4) = o1 * f;
+  if (a.lse && lane == 0)
+    a.lse[(int64_t)b * H + h] = tot > 0.0f ? (M + __log2f(tot)) * kLn2 : (tot != tot ? tot : -INFINITY);
+}
+
 // Launches; with profile events the kernel is launched through hipExtLaunchKernelGGL, which
 // records them at the kernel's own start and end.
 template <typename K>
@@ -868,6 +935,11 @@ static hipError_t launch(K kernel, dim3 grid, dim3 block, hipStream_t stream, hi
 // with hundreds of splits, 32-dim chunks (twice the lane groups, half the batches per
 // workgroup) were faster again (7.7 vs 8.2 us at 2 requests x 512 splits)
 static hipError_t launch_fmt_merge(const DecodeArgs& a, hipStream_t stream, hipEvent_t t0, hipEvent_t t1) {
+  if (a.part_splits <= kRowMergeMax) {
+    const int64_t rows = (int64_t)a.batch * a.num_heads;
+    return launch(mla_merge_rows_kernel, dim3((unsigned)((rows + kRowMergeRows - 1) / kRowMergeRows)),
+                  dim3(64 * kRowMergeRows), stream, t0, t1, a);
+  }
   if (a.batch * a.num_heads <= 256) {
     if (a.part_splits <= 64)
       return launch(mla_merge_kernel<128>, dim3(kDV / 128, a.num_heads, a.batch), dim3(kMergeThreads), stream, t0,
