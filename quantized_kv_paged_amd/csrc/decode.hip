@@ -253,9 +253,9 @@ __device__ __forceinline__ void fix_raw(RawTile<FMT>& r, int state) {
 }
 
 // MFMA operand of k-block KB of the lane's row half.  NVFP4: the 16-dim block of k-block
-// 4c + s is byte 2c + s/2 of s; one byte permutation gives bytes (2c, 2c, 2c + 1, 2c + 1), whose
-// low or high pair converts to that block's scale in both halves of an fp16 pair; the block of
-// k-block 8 is byte 2dh + g/2 of sr (selector ssel).
+// 4c + s is byte 2c + s/2 of s; bytes 2c and 2c + 1 convert together to an fp16 pair, and the
+// products take the block's half of it in both lanes of the pair (an operand select of the packed
+// multiply, no extra instruction); the block of k-block 8 is byte 2dh + g/2 of sr (selector ssel).
 template <int FMT, int KB>
 __device__ __forceinline__ typename OpType<FMT>::type dequant(const RawTile<FMT>& r, uint32_t ssel) {
   if constexpr (FMT == FMT_FP8) {
@@ -267,8 +267,8 @@ __device__ __forceinline__ typename OpType<FMT>::type dequant(const RawTile<FMT>
   } else if constexpr (FMT == FMT_NVFP4) {
     f16x2 s2;
     if constexpr (KB < 8) {
-      const uint32_t sb = __builtin_amdgcn_perm(r.s, r.s, (KB >> 2) ? 0x03030202u : 0x01010000u);
-      s2 = fp8x2_to_f16<((KB & 3) >= 2)>(sb);
+      const f16x2 sp = fp8x2_to_f16<((KB >> 2) != 0)>(r.s);
+      s2 = __builtin_shufflevector(sp, sp, (KB & 3) >> 1, (KB & 3) >> 1);
     } else {
       s2 = fp8x2_to_f16<false>(__builtin_amdgcn_perm(0u, r.sr, ssel));
     }
@@ -440,12 +440,11 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
       const BufferRsrc kv = make_rsrc(a.kv + rbase * kRowBytes, nvalid * kRowBytes);
       const BufferRsrc sc = make_rsrc(FMT == FMT_NVFP4 ? a.kv_scales + rbase * kNvScale : a.kv,
                                       FMT == FMT_NVFP4 ? nvalid * kNvScale : 0);
+      // the states of the lanes' rows are formed only for a tile with invalid rows (see compute);
+      // s[0] keeps the tile's count of valid rows
 #pragma unroll
-      for (int tb = 0; tb < kBlocks; ++tb) {
-        const int tt = my_tok + 16 * tb;
-        s[tb] = t0 + tt >= t_end ? 1 : (tt >= nvalid ? 2 : 0);
-        load_raw_tile<FMT>(r[tb], kv, sc, lofs, dh, grp, 16 * tb);
-      }
+      for (int tb = 0; tb < kBlocks; ++tb) load_raw_tile<FMT>(r[tb], kv, sc, lofs, dh, grp, 16 * tb);
+      s[0] = nvalid;
     } else {
 #pragma unroll
       for (int tb = 0; tb < kBlocks; ++tb) {
@@ -469,9 +468,10 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
 #pragma unroll
     for (int kb = 0; kb < 9; ++kb) qop[kb] = __builtin_bit_cast(bf16x8, qraw[kb]);
   } else {
-    // exact bf16 -> fp16 with a power-of-two prescale 2^s per (head, dim half) chosen so that
-    // max|q| < 2^16 (the 4 lane groups of a head are the 4 rows of the wave); 2^-s goes into
-    // the score scale of this half's partial scores
+    // exact bf16 -> fp16 with a power-of-two prescale 2^s per head chosen so that max|q| < 2^16
+    // over both dim halves (the 4 lane groups of a head are the 4 rows of the wave; the pair
+    // partners exchange their halves' maxima through the swap buffer that tile 1 uses first);
+    // 2^-s goes into the score scale, which is then the same for both halves' partial scores
     uint32_t mx = 0;
 #pragma unroll
     for (int kb = 0; kb < 9; ++kb)
@@ -480,7 +480,13 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
         const uint32_t v = qraw[kb][e];
         mx = max(mx, max((v & 0x7fffu) << 16, v & 0x7fff0000u));
       }
-    const float qmax = rows_max(u2f(mx));
+    float qmax = rows_max(u2f(mx));
+    {
+      float* const sX0 = reinterpret_cast<float*>(smem + kSwap);
+      if (lane < 16) sX0[(kWaves + w) * (kSwapW / 4) + lane] = qmax;
+      __syncthreads();
+      qmax = fmaxf(qmax, sX0[(kWaves + (w ^ kStreams)) * (kSwapW / 4) + l16]);
+    }
     const int ex = (int)((f2u(qmax) >> 23) & 0xff) - 127;       // floor(log2 max|q|)
     const int sh = (qmax == 0.0f || ex >= 128) ? 0 : min(15 - ex, 64);   // in [-112, 64]
     const float up = u2f((uint32_t)(127 + sh) << 23);
@@ -522,9 +528,21 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
   // pair partner, online softmax of the stream, O += P V over the wave's dim half.
   auto compute = [&](RawTile<FMT>(&cur)[kBlocks], int(&st)[kBlocks], int t0, int buf, bool more)
                      __attribute__((always_inline)) {
+    if constexpr (TILEPAGE) {
+      const int nvalid = __builtin_amdgcn_readfirstlane(st[0]);
+      if (t0 + kTile > t_end || nvalid < kTile) {   // uniform: rows past the chunk or outside the pool
 #pragma unroll
-    for (int tb = 0; tb < kBlocks; ++tb)
-      if (__any(st[tb] != 0)) fix_raw<FMT>(cur[tb], st[tb]);
+        for (int tb = 0; tb < kBlocks; ++tb) {
+          const int tt = my_tok + 16 * tb;
+          const int state = t0 + tt >= t_end ? 1 : (tt >= nvalid ? 2 : 0);
+          if (__any(state != 0)) fix_raw<FMT>(cur[tb], state);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int tb = 0; tb < kBlocks; ++tb)
+        if (__any(st[tb] != 0)) fix_raw<FMT>(cur[tb], st[tb]);
+    }
     f32x4 sacc[kBlocks];
 #pragma unroll
     for (int tb = 0; tb < kBlocks; ++tb) sacc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -557,10 +575,11 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
     // waits; the score swap runs at 1, the softmax and PV (latency-bound) at 0
     __builtin_amdgcn_s_setprio(1);
     if (more) fetch(cur, st, t0 + kTile);
-    // lane: head l16, tokens 32tg + 16tb + 4grp + i
+    // lane: head l16, tokens 32tg + 16tb + 4grp + i (partial sums of this dim half, unscaled:
+    // both halves share the head's score scale, applied once to their sum)
     f32x4 sp[kBlocks];
 #pragma unroll
-    for (int tb = 0; tb < kBlocks; ++tb) sp[tb] = sacc[tb] * score_scale;
+    for (int tb = 0; tb < kBlocks; ++tb) sp[tb] = sacc[tb];
     if (t0 + kTile > t_end) {   // partial tile (uniform)
 #pragma unroll
       for (int tb = 0; tb < kBlocks; ++tb)
@@ -613,8 +632,8 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
     float lmax = sc[0];
 #pragma unroll
     for (int j = 1; j < 4 * kBlocks; ++j) lmax = fmaxf(lmax, sc[j]);
-    if (__any(lmax > m_run + kSlack)) {
-      const float tmax = rows_max(lmax);
+    if (__any(lmax * score_scale > m_run + kSlack)) {
+      const float tmax = rows_max(lmax) * score_scale;
       const bool grow = tmax > m_run + kSlack;
       const float m_new = grow ? tmax : m_run;
       const float alpha = fast_exp2(m_run - m_new);
@@ -630,23 +649,21 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
     // P in the A-operand layout of the 32-token product: lane (g, head l16) holds k-indices
     // 8g .. 8g+7 = tokens 4g .. 4g+3 of block 0, then 4g .. 4g+3 of block 1
     Op pop;
-    float rsum = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4 * kBlocks; ++j) {
       // the sum takes the rounded probabilities the products use, so that the output is a
       // convex combination of value rows (rows with equal values reproduce them exactly)
-      const float pe = fast_exp2(sc[j] - m_run);
+      const float pe = fast_exp2(__builtin_fmaf(sc[j], score_scale, -m_run));
       if constexpr (FMT == FMT_BF16) pop[j] = (__bf16)pe;
       else pop[j] = (_Float16)pe;
     }
 #pragma unroll
-    for (int j = 0; j < 4 * kBlocks; j += 2) {    // sum of the rounded pairs, one dot2 per pair
+    for (int j = 0; j < 4 * kBlocks; j += 2) {    // the rounded pairs added to the sum, one dot2 per pair
       if constexpr (FMT == FMT_BF16)
-        rsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pop[j], pop[j + 1]}, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, rsum, false);
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pop[j], pop[j + 1]}, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, l_run, false);
       else
-        rsum = __builtin_amdgcn_fdot2(f16x2{pop[j], pop[j + 1]}, f16x2{(_Float16)1.0f, (_Float16)1.0f}, rsum, false);
+        l_run = __builtin_amdgcn_fdot2(f16x2{pop[j], pop[j + 1]}, f16x2{(_Float16)1.0f, (_Float16)1.0f}, l_run, false);
     }
-    l_run += rsum;
     // O += P V: 16 dims per product, K = this group's 32 tokens.  The operands are read in
     // batches of kVAhead dim blocks, each batch issued before the products of the previous
     // one (scheduling barriers keep the compiler from shortening that distance, so a product
