@@ -175,6 +175,12 @@ mlaq_status decode_common(int fmt, const mlaq_decode_params* p, const uint16_t* 
   a.num_heads = p->num_heads;
   a.page_size = p->page_size;
   a.page_shift = __builtin_ctz((unsigned)p->page_size);
+  {
+    const int64_t pages = p->pool_tokens >> a.page_shift;
+    const bool huge = pages >= (int64_t)std::numeric_limits<int32_t>::max();
+    a.pool_pages = huge ? std::numeric_limits<int32_t>::max() : (int32_t)pages;
+    a.pool_tail = huge ? p->page_size : (int32_t)(p->pool_tokens & (p->page_size - 1));
+  }
   a.max_kv_len = p->max_kv_len;
   a.num_splits = splits;
   a.part_splits = part_splits;

@@ -432,11 +432,14 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
       // all lanes share the page: the tile's valid rows (tokens before t_end, rows inside the
       // pool) are rows row0 .. row0 + nvalid - 1; lanes of other rows read zeros through the
       // descriptors' size limit, which fix_raw keeps (past the chunk) or replaces by NaN codes
+      // (a whole page of the pool holds the tile, which never straddles pages; the pool's partial
+      // last page holds pool_tail rows; any other id holds none)
       const int page = pw.page<true>(a, t0, lane);
-      const int64_t row0 = ((int64_t)page << a.page_shift) + (t0 & (a.page_size - 1));
-      const int64_t room = page >= 0 ? a.pool_tokens - row0 : 0;
-      const int nvalid = (int)max((int64_t)0, min((int64_t)min(kTile, t_end - t0), room));
-      const int64_t rbase = nvalid > 0 ? row0 : 0;
+      const int off = t0 & (a.page_size - 1);
+      const int want = min(kTile, t_end - t0);
+      const int nvalid = (unsigned)page < (unsigned)a.pool_pages ? want
+                         : page == a.pool_pages ? max(0, min(want, a.pool_tail - off)) : 0;
+      const int64_t rbase = nvalid > 0 ? ((int64_t)page << a.page_shift) + off : 0;
       const BufferRsrc kv = make_rsrc(a.kv + rbase * kRowBytes, nvalid * kRowBytes);
       const BufferRsrc sc = make_rsrc(FMT == FMT_NVFP4 ? a.kv_scales + rbase * kNvScale : a.kv,
                                       FMT == FMT_NVFP4 ? nvalid * kNvScale : 0);

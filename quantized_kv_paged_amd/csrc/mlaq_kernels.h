@@ -34,6 +34,10 @@ struct DecodeArgs {
   int32_t batch, num_heads, page_size, max_kv_len, num_splits, chunk_tokens;
   int32_t part_splits;        // partial slots per (request, head group): num_splits (+ 1 with a fused append)
   int32_t page_shift;         // log2(page_size) (page sizes are powers of two)
+  // pool pages for the page-tile check: ids in [0, pool_pages) are whole pages of the pool, and
+  // page id pool_pages holds pool_tail rows (0: none); with more than 2^31 - 1 pages, every
+  // non-negative id is a whole page (pool_pages = 2^31 - 1, pool_tail = page_size)
+  int32_t pool_pages, pool_tail;
   float score_scale;          // sm_scale * (kv scale or global scale) * log2(e)
   float out_scale;            // kv scale or global scale
   // fused append (NVFP4 only): the last token of every request is the new row app_src[b],

@@ -267,3 +267,37 @@ def test_peaked_softmax_with_long_tail(fmt):
     with pytest.raises(qk.MlaqError) as e:
         gpu_decode(c, d, num_splits=least - 1)
     assert e.value.status == 2
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "nvfp4"])
+def test_page_tiles_at_the_pool_edge(fmt):
+    """Pages that hold whole tiles (64 tokens): the pool ends 40 rows into its last page.  A request
+    whose last page is that partial page and whose rows stay inside the pool is exact; one that
+    reads past the pool's end, one with a page id just past the pool and one with a negative page
+    id give NaN, in single-split and automatic-split launches."""
+    P = 64
+    c = build_case(fmt, [64 * 3 + 38, 64 * 2 + 50, 64 * 4, 64 * 2 + 7, 64 * 5], P, seed=41, extra_pages=4)
+    n_pages = c.w.pool_tokens // P
+    last = n_pages - 1
+    T = last * P + 40                                    # pool rows: the last page holds 40
+    idx = c.pt.kv_indices.copy()
+    ip = c.pt.kv_indptr
+    free = [p for p in range(n_pages) if p not in set(idx.tolist()) and p != last]
+    for k in np.nonzero(idx == last)[0]:                 # only requests 0 and 1 use the partial page
+        idx[k] = free.pop()
+    idx[ip[1] - 1] = last                                # request 0: 38 of its 40 rows
+    idx[ip[2] - 1] = last                                # request 1: 50 rows, 10 past the pool's end
+    idx[ip[2] + 1] = n_pages                             # request 2: a page id past the pool
+    idx[ip[3]] = -1                                      # request 3: a negative page id
+    c.pt.kv_indices = idx
+    ref_out, ref_lse = oracle_decode(c, requests=[0, 4])
+    d = Device(c)
+    if fmt == "fp8":
+        d.fp8 = d.fp8[:T].contiguous()
+    else:
+        d.nv_data, d.nv_scales = d.nv_data[:T].contiguous(), d.nv_scales[:T].contiguous()
+    for s in (1, 0):
+        out, lse = gpu_decode(c, d, num_splits=s)
+        for b in (1, 2, 3):
+            assert np.isnan(out[b]).all() and np.isnan(lse[b]).all(), (s, b)
+        assert_parity(out, lse, ref_out, ref_lse, requests=[0, 4], tag=f"pool edge {fmt} splits={s}")
