@@ -426,28 +426,37 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
   const LaneOffsets lofs = lane_offsets<FMT>(my_tok, dh, grp);
   constexpr int kRowBytes = FMT == FMT_FP8 ? kD : FMT == FMT_NVFP4 ? kNvData : 2 * kD;
   // loads of the lane's share of tile t0 (both blocks) into r, validity states into s
-  // (0 valid, 1 past the chunk, 2 no valid row; see tile_row)
+  // (0 valid, 1 past the chunk, 2 no valid row; see tile_row).  With pages of at least a tile,
+  // all lanes share the page: the tile's valid rows (tokens before t_end, rows inside the pool)
+  // are rows row0 .. row0 + nvalid - 1, and lanes of other rows read zeros through the
+  // descriptors' size limit, which fix_raw keeps (past the chunk) or replaces by NaN codes (a
+  // whole page of the pool holds the tile, which never straddles pages; the pool's partial last
+  // page holds pool_tail rows; any other id holds none).  The descriptors are formed apart from
+  // the loads, so that their scalar chain can run beside the previous tile's conversion.
+  struct TileDesc { BufferRsrc kv, sc; int nvalid; };
+  auto tile_desc = [&](int t0) __attribute__((always_inline)) {
+    const int page = pw.page<true>(a, t0, lane);
+    const int off = t0 & (a.page_size - 1);
+    const int want = max(0, min(kTile, t_end - t0));
+    const int nvalid = (unsigned)page < (unsigned)a.pool_pages ? want
+                       : page == a.pool_pages ? max(0, min(want, a.pool_tail - off)) : 0;
+    const int64_t rbase = nvalid > 0 ? ((int64_t)page << a.page_shift) + off : 0;
+    TileDesc d;
+    d.kv = make_rsrc(a.kv + rbase * kRowBytes, nvalid * kRowBytes);
+    d.sc = make_rsrc(FMT == FMT_NVFP4 ? a.kv_scales + rbase * kNvScale : a.kv, FMT == FMT_NVFP4 ? nvalid * kNvScale : 0);
+    d.nvalid = nvalid;
+    return d;
+  };
+  // (page tiles: the states of the lanes' rows are formed only for a tile with invalid rows, see
+  // compute; s[0] keeps the tile's count of valid rows)
+  auto issue = [&](RawTile<FMT>(&r)[kBlocks], int(&s)[kBlocks], const TileDesc& d) __attribute__((always_inline)) {
+#pragma unroll
+    for (int tb = 0; tb < kBlocks; ++tb) load_raw_tile<FMT>(r[tb], d.kv, d.sc, lofs, dh, grp, 16 * tb);
+    s[0] = d.nvalid;
+  };
   auto fetch = [&](RawTile<FMT>(&r)[kBlocks], int(&s)[kBlocks], int t0) __attribute__((always_inline)) {
     if constexpr (TILEPAGE) {
-      // all lanes share the page: the tile's valid rows (tokens before t_end, rows inside the
-      // pool) are rows row0 .. row0 + nvalid - 1; lanes of other rows read zeros through the
-      // descriptors' size limit, which fix_raw keeps (past the chunk) or replaces by NaN codes
-      // (a whole page of the pool holds the tile, which never straddles pages; the pool's partial
-      // last page holds pool_tail rows; any other id holds none)
-      const int page = pw.page<true>(a, t0, lane);
-      const int off = t0 & (a.page_size - 1);
-      const int want = min(kTile, t_end - t0);
-      const int nvalid = (unsigned)page < (unsigned)a.pool_pages ? want
-                         : page == a.pool_pages ? max(0, min(want, a.pool_tail - off)) : 0;
-      const int64_t rbase = nvalid > 0 ? ((int64_t)page << a.page_shift) + off : 0;
-      const BufferRsrc kv = make_rsrc(a.kv + rbase * kRowBytes, nvalid * kRowBytes);
-      const BufferRsrc sc = make_rsrc(FMT == FMT_NVFP4 ? a.kv_scales + rbase * kNvScale : a.kv,
-                                      FMT == FMT_NVFP4 ? nvalid * kNvScale : 0);
-      // the states of the lanes' rows are formed only for a tile with invalid rows (see compute);
-      // s[0] keeps the tile's count of valid rows
-#pragma unroll
-      for (int tb = 0; tb < kBlocks; ++tb) load_raw_tile<FMT>(r[tb], kv, sc, lofs, dh, grp, 16 * tb);
-      s[0] = nvalid;
+      issue(r, s, tile_desc(t0));
     } else {
 #pragma unroll
       for (int tb = 0; tb < kBlocks; ++tb) {
@@ -531,6 +540,13 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
   // pair partner, online softmax of the stream, O += P V over the wave's dim half.
   auto compute = [&](RawTile<FMT>(&cur)[kBlocks], int(&st)[kBlocks], int t0, int buf, bool more)
                      __attribute__((always_inline)) {
+    // the next tile's descriptors, formed here (pinned by an empty use) so that their scalar
+    // chain runs while the wave waits for this tile's rows rather than after the conversion
+    TileDesc nd;
+    if constexpr (TILEPAGE) {
+      nd = tile_desc(t0 + kTile);
+      asm volatile("" ::"s"(nd.kv), "s"(nd.sc));
+    }
     if constexpr (TILEPAGE) {
       const int nvalid = __builtin_amdgcn_readfirstlane(st[0]);
       if (t0 + kTile > t_end || nvalid < kTile) {   // uniform: rows past the chunk or outside the pool
@@ -577,7 +593,10 @@ __global__ __launch_bounds__(Geo<NS>::kThreads, 2) void mla_decode_kernel(Decode
     // the other wave of the SIMD (of another workgroup) fills its gaps only while this one
     // waits; the score swap runs at 1, the softmax and PV (latency-bound) at 0
     __builtin_amdgcn_s_setprio(1);
-    if (more) fetch(cur, st, t0 + kTile);
+    if (more) {
+      if constexpr (TILEPAGE) issue(cur, st, nd);
+      else fetch(cur, st, t0 + kTile);
+    }
     // lane: head l16, tokens 32tg + 16tb + 4grp + i (partial sums of this dim half, unscaled:
     // both halves share the head's score scale, applied once to their sum)
     f32x4 sp[kBlocks];
