@@ -185,7 +185,7 @@ mlaq_status mla_decode_nvfp4_append(const mlaq_decode_params* p, const uint16_t*
  * round to 4), the chunk's FP8 rows are appended, attention runs over that workspace, and
  * the chunk is then quantized into the cache at slot_mapping[t] (kv_quantize_nvfp4 with
  * src_scale = chunk_scale; rows < 0 skipped).  The attention reads each workspace row once
- * per four chunk tokens and 16-head group, on MFMA; KV splits of long prefixes are merged
+ * per eight chunk tokens and 16-head group, on MFMA; KV splits of long prefixes are merged
  * like the decode splits.
  *   q          bf16 [num_q, num_heads, 576]      chunk_kv  e4m3fn [num_q, 576], x = e4m3 * chunk_scale
  *   qo_indptr  int32 [batch + 1]                  prefix_lens int32 [batch]
