@@ -177,7 +177,7 @@ mlaq_status decode_common(int fmt, const mlaq_decode_params* p, const uint16_t* 
   a.page_shift = __builtin_ctz((unsigned)p->page_size);
   {
     const int64_t pages = p->pool_tokens >> a.page_shift;
-    const bool huge = pages >= (int64_t)std::numeric_limits<int32_t>::max();
+    const bool huge = pages > (int64_t)std::numeric_limits<int32_t>::max();   // else id 2^31 - 1 may be the partial page
     a.pool_pages = huge ? std::numeric_limits<int32_t>::max() : (int32_t)pages;
     a.pool_tail = huge ? p->page_size : (int32_t)(p->pool_tokens & (p->page_size - 1));
   }
