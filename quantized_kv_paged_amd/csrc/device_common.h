@@ -125,6 +125,20 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_rne_sat(float x) {
   return sign | ((uint32_t)(e + 7) << 3) + ((uint32_t)q - 8u);
 }
 
+// Two fp32 values -> two e4m3fn bytes (lo in bits 0-7, hi in bits 8-15), the same bytes as
+// f32_to_e4m3_rne_sat.  gfx950's fp8 conversion rounds to nearest even like it for every
+// magnitude up to 464 but gives NaN above that, and NaN inputs come out as 0xFF; so the inputs
+// are clamped to +-448 first (RNE takes (448, 464] to 448 as well) and NaN inputs get 0x7F.
+// Checked on the GPU against f32_to_e4m3_rne_sat for every fp32 bit pattern.
+__device__ __forceinline__ uint32_t f32x2_to_e4m3(float lo, float hi) {
+  const float cl = __builtin_amdgcn_fmed3f(lo, -448.0f, 448.0f);
+  const float ch = __builtin_amdgcn_fmed3f(hi, -448.0f, 448.0f);
+  uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(cl, ch, 0, false) & 0xffffu;
+  w = lo != lo ? (w & 0xff00u) | 0x7fu : w;
+  w = hi != hi ? (w & 0x00ffu) | 0x7f00u : w;
+  return w;
+}
+
 // Two fp32 values -> two E2M1 nibbles (low nibble = lo) written to byte SEL of w: round to
 // nearest even on {0, .5, 1, 1.5, 2, 3, 4, 6}, saturating, sign kept (-0 -> 0x8).  gfx950's
 // scaled fp4 conversion at scale 1.0 rounds exactly this way: it gave the same nibble as the

@@ -78,11 +78,8 @@ __global__ __launch_bounds__(256) void extend_gather_kernel(ExtendArgs a) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = v[i] / a.chunk_scale;
       }
-      uint32_t e[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) e[i] = f32_to_e4m3_rne_sat(v[i]);
-      o[2 * h] = e[0] | (e[1] << 8) | (e[2] << 16) | (e[3] << 24);
-      o[2 * h + 1] = e[4] | (e[5] << 8) | (e[6] << 16) | (e[7] << 24);
+      o[2 * h] = f32x2_to_e4m3(v[0], v[1]) | (f32x2_to_e4m3(v[2], v[3]) << 16);
+      o[2 * h + 1] = f32x2_to_e4m3(v[4], v[5]) | (f32x2_to_e4m3(v[6], v[7]) << 16);
     }
     dst[blk] = u32x4{o[0], o[1], o[2], o[3]};
   }

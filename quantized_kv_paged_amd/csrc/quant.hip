@@ -89,8 +89,7 @@ __global__ __launch_bounds__(256) void dequantize_kernel(DequantArgs a) {
     u32x4 o;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      o[e] = f32_to_e4m3_rne_sat(v[4 * e]) | (f32_to_e4m3_rne_sat(v[4 * e + 1]) << 8) |
-             (f32_to_e4m3_rne_sat(v[4 * e + 2]) << 16) | (f32_to_e4m3_rne_sat(v[4 * e + 3]) << 24);
+      o[e] = f32x2_to_e4m3(v[4 * e], v[4 * e + 1]) | (f32x2_to_e4m3(v[4 * e + 2], v[4 * e + 3]) << 16);
     *reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(a.dst) + r * kD + 16 * k) = o;
   }
 }
