@@ -207,6 +207,32 @@ def test_dequantize_nvfp4_bit_exact(g):
     assert np.isnan(qk.kv_dequantize(qk.MLAQ_NVFP4, d, s, g, qk.MLAQ_FP32, rows=_t(rows)).cpu().numpy()[10]).all()
 
 
+@pytest.mark.parametrize("g", [1.0, 1.02])
+def test_dequantize_nvfp4_to_fp8_saturates_bit_exact(g):
+    """FP8 output of values past the e4m3 range, byte for byte as the oracle's encoder gives them:
+    rows of magnitude up to about 700 dequantize to values above 464, which saturate to +-448
+    (0x7E / 0xFE); at g = 1.02 products such as 448 g = 456.96 land in (448, 464], which round to
+    448; a NaN block scale gives the NaN code 0x7F in all 16 bytes of its block."""
+    qk = _qk()
+    rng = np.random.default_rng(47)
+    n = 64
+    x = (rng.standard_normal((n, 576)) * 150).astype(np.float32)
+    x[7, 64:80] = 0.0
+    x[7, 64:66] = [685.44, 457.0]   # block scale 685.44 / 6 / 1.02 = 112; 457 codes as 4: 448 g
+    d_np, s_np = onv.quantize_rows(x, g)
+    s_np[5, 2] = 0x7F                                    # NaN scale: dims 32 .. 47 of row 5
+    f32 = onv.dequant_nvfp4_f32(d_np, s_np, g)
+    ref = onv.e4m3_encode_array(f32)
+    out = qk.kv_dequantize(qk.MLAQ_NVFP4, _t(d_np), _t(s_np), g, qk.MLAQ_FP8_E4M3)
+    got = out.cpu().numpy()
+    np.testing.assert_array_equal(got, ref)
+    assert (got == 0x7E).any() and (got == 0xFE).any()   # saturated codes were produced
+    assert (got[5, 32:48] == 0x7F).all()
+    if g != 1.0:
+        a = np.abs(f32[~np.isnan(f32)])
+        assert ((a > 448) & (a <= 464)).any()            # the round-to-448 interval was reached
+
+
 def test_dequantize_fp8_bit_exact():
     qk = _qk()
     codes = np.tile(np.arange(256, dtype=np.uint8), 9 * 40).reshape(160, 576)
